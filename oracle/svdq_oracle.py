@@ -1,0 +1,356 @@
+"""CPU oracle for the SVDQuant W4A4 linear layer with its low-rank branch.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+CPU-baseline leg of the benchmark may import this module.  The product path
+(the HIP library and its Python binding) never calls it, and it shares no
+code, tables or helpers with that path.
+
+It is plain, slow and written to be checked by eye against the pages:
+numpy in float64, except at the points where the method itself fixes a
+float32 rounding (smoothing, quantization scales, codes), where numpy's
+IEEE float32 arithmetic is used.  Citations name the page and the section
+or equation:
+
+  [Term] "SVDQuant Low-Rank Residual Quantization Algorithm Terminology
+         Entry" (mindstudio docs), section 2.3 "Mathematical Description":
+         (E1) outlier migration  Y = XW + b = (X diag(s)^-1)(diag(s) W) + b
+         (E2) s = A_scale^alpha / W_scale^(1-alpha),  s >= s_min
+         (E3) W ~ (U S) V^T,  R = W - (U S) V^T
+         (E4) out = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 V)(U S)^T ~ XW + b
+         (E5) Eckart-Young: the truncated SVD is the best rank-r approximation
+         (E6) residual energy = sum of the squared tail singular values
+         (E7) XW^T = X L_r^T + X R^T, low-bit only for R
+  [Abs]  "SVDQuant: Absorbing Outliers by Low-Rank Components for 4-Bit
+         Diffusion Models" (codewithpapers abstract): 4-bit weights and
+         activations, high-precision low-rank branch.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+  weights are stored [N, K] (out, in) and s indexes input channels k;
+  W_scale is the per-input-channel absolute maximum;
+  s_min = 1e-5 and both statistics are floored at 1e-5 before the power;
+  the low-rank factors are L1 = V_r (lora_down, [K, r]) and
+  L2 = (U_r Sigma_r)^T (lora_up, [r, N]), both rounded to bfloat16;
+  R is formed from the rounded factors;
+  Q is symmetric 4-bit, one float32 scale per 64 consecutive input channels,
+  scale = fl32(amax / 7), codes = clamp(rne(fl32(v * fl32(7 / amax))), -7, 7),
+  an all-zero group gets scale 0 and codes 0;
+  a weight scale additionally has its two lowest significand bits cleared
+  (rounded toward zero), so that 3 * scale is exact in float32;
+  x_hat = fl32(X * fl32(1 / s));
+  codes are packed two per byte, the even channel in the low nibble.
+
+Parity status: every function below has at least one pin in
+tests/test_oracle_pins.py that does not re-type its formula.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 64
+QMAX = 7
+S_MIN = 1e-5
+STAT_FLOOR = 1e-5
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ---------------------------------------------------------------- bfloat16
+def bf16_from_f64(x) -> np.ndarray:
+    """Round float64 values straight to bfloat16 (nearest, ties to even).
+
+    Returns uint16 bit patterns.  Works on the exact binary value: the
+    significand is cut to 8 bits with one rounding, no detour via float32.
+    """
+    x = np.asarray(x, dtype=F64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.ravel()
+    flat_out = out.ravel()
+    for i, v in enumerate(flat_in):
+        flat_out[i] = _bf16_scalar(float(v))
+    return out
+
+
+def _bf16_scalar(v: float) -> int:
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    m, e = math.frexp(a)            # a = m * 2^e, m in [0.5, 1)
+    # bfloat16 normal numbers: 8 significant bits, exponent of the leading bit >= -126
+    lead = e - 1                    # a in [2^lead, 2^(lead+1))
+    bits_exp = max(lead, -126)      # subnormal range keeps the -126 exponent grid
+    ulp = math.ldexp(1.0, bits_exp - 7)
+    q = a / ulp                     # exact: a power-of-two division
+    r = math.floor(q)
+    frac = q - r
+    if frac > 0.5 or (frac == 0.5 and (r % 2 == 1)):
+        r += 1
+    val = r * ulp
+    if val >= math.ldexp(1.0, 128):  # overflow to infinity
+        return sign | 0x7F80
+    # encode val (exactly a bfloat16) through float32 bits
+    return sign | int(np.array(val, dtype=F32).view(np.uint32) >> 16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(F32).astype(F64)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(F32)
+
+
+# ---------------------------------------------------- stage one: smoothing
+def act_absmax(xcal_bf16) -> np.ndarray:
+    """A_scale[k]: absolute maximum of each input channel over the calibration rows.
+
+    [Term] 2.3, the definition of A_scale under (E2).  Exact (float32 max).
+    """
+    return np.max(np.abs(bf16_to_f32(xcal_bf16)), axis=0)
+
+
+def weight_absmax(W) -> np.ndarray:
+    """W_scale[k]: absolute maximum over output rows of input channel k.
+
+    [Term] 2.3, W_scale under (E2) ("per-column maximum"; W is stored [N, K]
+    here, so the column of the page's [in, out] W is our input channel).
+    """
+    return np.max(np.abs(np.asarray(W, dtype=F32)), axis=0)
+
+
+def smoothing_factors(A, Wsc, alpha: float = 0.5, s_min: float = S_MIN) -> np.ndarray:
+    """s[k] = max(A^alpha / W_scale^(1-alpha), s_min), evaluated in float64, stored float32.
+
+    [Term] 2.3 (E2).  Plain per-element libm pow.
+    """
+    A = np.asarray(A, dtype=F64)
+    Wsc = np.asarray(Wsc, dtype=F64)
+    s = np.empty(A.shape, dtype=F64)
+    for k in range(A.shape[0]):
+        a = max(float(A[k]), STAT_FLOOR)
+        w = max(float(Wsc[k]), STAT_FLOOR)
+        s[k] = max(math.pow(a, alpha) / math.pow(w, 1.0 - alpha), s_min)
+    return s.astype(F32)
+
+
+def smooth_weight(W, s) -> np.ndarray:
+    """W_hat = W diag(s) (each input channel k scaled by s[k]), exact in float64.
+
+    [Term] 2.3 (E1): the weight side of the outlier migration.
+    """
+    return np.asarray(W, dtype=F32).astype(F64) * np.asarray(s, dtype=F32).astype(F64)[None, :]
+
+
+# --------------------------------------------- stage two: low-rank branch
+def svd_sorted(What):
+    """Thin SVD W_hat = U diag(sigma) V^T, sigma descending.
+
+    [Term] 2.2 and 2.3 (E3).  numpy's LAPACK SVD is the library step; the
+    sign of each pair is fixed so that the largest-magnitude entry of v_i
+    is positive (any sign is a valid SVD; this just makes runs repeatable).
+    Returns U [N, p], sigma [p], V [K, p].
+    """
+    U, S, Vt = np.linalg.svd(np.asarray(What, dtype=F64), full_matrices=False)
+    order = np.argsort(-S, kind="stable")
+    U, S, V = U[:, order], S[order], Vt[order, :].T
+    idx = np.argmax(np.abs(V), axis=0)
+    sgn = np.sign(V[idx, np.arange(V.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return U * sgn[None, :], S, V * sgn[None, :]
+
+
+def lowrank_factors(U, S, V, r: int):
+    """L1 = bf16(V_r) [K, r] (lora_down), L2 = bf16((U_r Sigma_r)^T) [r, N] (lora_up).
+
+    [Term] 2.3 (E4): the branch is (X diag(s)^-1 V)(U S)^T, so Sigma rides
+    with U.  Returns uint16 bfloat16 bit patterns.
+    """
+    L1 = bf16_from_f64(V[:, :r])
+    L2 = bf16_from_f64((U[:, :r] * S[None, :r]).T)
+    return L1, L2
+
+
+def residual(What, L1_bf16, L2_bf16) -> np.ndarray:
+    """R = fl32(W_hat - L1 L2) with R[n, k] = W_hat[n, k] - sum_j L1[k, j] L2[j, n].
+
+    [Term] 2.3 (E3) with the stored (rounded) factors.  The inner sum runs
+    over j in ascending order in float64 starting from 0, each product exact
+    (bfloat16 x bfloat16), then one subtraction and one rounding to float32.
+    """
+    What = np.asarray(What, dtype=F64)
+    L1 = bf16_to_f64(L1_bf16)
+    L2 = bf16_to_f64(L2_bf16)
+    r = L1.shape[1] if L1.ndim == 2 else 0
+    acc = np.zeros(What.shape, dtype=F64)
+    for j in range(r):
+        acc += L2[j, :][:, None] * L1[:, j][None, :]
+    return (What - acc).astype(F32)
+
+
+# ------------------------------------------- stage three: quantization Q
+def quantize_groups(v32, weight_scale: bool = False):
+    """Q(.) over groups of 64 consecutive entries of the last axis.
+
+    [Term] 2.3 (E4) names Q; [Abs] fixes 4 bits.  Symmetric, codes in
+    [-7, 7]:  a = max|v|;  scale = fl32(a / 7);  inv = fl32(7 / a);
+    q = clamp(rne(fl32(v * inv)), -7, 7).  a == 0 gives scale 0, q 0.
+    weight_scale=True clears the two lowest significand bits of the scale.
+    Returns (codes int8 [..., K], scales float32 [..., K/64]).
+    """
+    v = np.asarray(v32, dtype=F32)
+    K = v.shape[-1]
+    assert K % GROUP == 0
+    g = v.reshape(v.shape[:-1] + (K // GROUP, GROUP))
+    a = np.max(np.abs(g), axis=-1)
+    nz = a > 0
+    safe = np.where(nz, a, F32(1))
+    scale = np.where(nz, safe / F32(QMAX), F32(0)).astype(F32)
+    inv = np.where(nz, F32(QMAX) / safe, F32(0)).astype(F32)
+    q = np.rint(g * inv[..., None])
+    q = np.clip(q, -QMAX, QMAX).astype(np.int8)
+    if weight_scale:
+        scale = (scale.view(np.uint32) & np.uint32(0xFFFFFFFC)).view(F32)
+    return q.reshape(v.shape), scale
+
+
+def pack_nibbles(q) -> np.ndarray:
+    """Two codes per byte: byte i = (q[2i] & 0xF) | (q[2i+1] & 0xF) << 4."""
+    q = np.asarray(q, dtype=np.int8).astype(np.int16)
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b) -> np.ndarray:
+    """Inverse of pack_nibbles: uint8 [..., K/2] -> int8 codes [..., K]."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# --------------------------------------------------------- offline pack
+def pack_weights(W, A, alpha: float = 0.5, rank: int = 32, s_min: float = S_MIN):
+    """The whole offline pipeline: smoothing, truncated SVD, residual quantization.
+
+    [Term] 2.1 (three stages in this order) and 2.3 (E1)-(E4).
+    Returns a dict with s, L1, L2 (bf16 bits), Wq (packed), w_scales, sigma,
+    and the float64 W_hat and float32 R for tests.
+    """
+    Wsc = weight_absmax(W)
+    s = smoothing_factors(A, Wsc, alpha, s_min)
+    What = smooth_weight(W, s)
+    U, S, V = svd_sorted(What)
+    L1, L2 = lowrank_factors(U, S, V, rank)
+    R = residual(What, L1, L2)
+    q, ws = quantize_groups(R, weight_scale=True)
+    return dict(s=s, L1=L1, L2=L2, Wq=pack_nibbles(q), w_scales=ws, sigma=S,
+                What=What, R=R, U=U, V=V)
+
+
+def quantize_residual(W, s, L1, L2):
+    """Wq and w_scales from given s, L1, L2 (the last two steps of pack_weights)."""
+    R = residual(smooth_weight(W, s), L1, L2)
+    q, ws = quantize_groups(R, weight_scale=True)
+    return pack_nibbles(q), ws
+
+
+# ------------------------------------------------------------- forward
+def smooth_activations(X_bf16, s) -> np.ndarray:
+    """x_hat = fl32(X * fl32(1 / s)), float32 [M, K].  [Term] 2.3 (E1), (E4)."""
+    inv_s = (F32(1) / np.asarray(s, dtype=F32)).astype(F32)
+    return (bf16_to_f32(X_bf16) * inv_s[None, :]).astype(F32)
+
+
+def quantize_activations(X_bf16, s, L1_bf16=None):
+    """First half of (E4): Q(X diag(s)^-1) and the lora_down product T = x_hat L1.
+
+    Returns (qx packed uint8 [M, K/2], sx float32 [M, K/64], T float64 [M, r], x_hat).
+    """
+    xh = smooth_activations(X_bf16, s)
+    q, sx = quantize_groups(xh)
+    if L1_bf16 is None or np.asarray(L1_bf16).size == 0:
+        T = np.zeros((xh.shape[0], 0), dtype=F64)
+    else:
+        T = xh.astype(F64) @ bf16_to_f64(L1_bf16)
+    return pack_nibbles(q), sx, T, xh
+
+
+def group_partials(qx_packed, wq_packed) -> np.ndarray:
+    """P[m, n, g] = sum over k in group g of qx[m, k] * qw[n, k], exact int32.
+
+    [Term] 2.3 (E4) the product Q(.)Q(R), (E7) low-bit only for R.  The
+    integer dot products are evaluated as float64 matrix products, which
+    are exact here (every partial sum is an integer below 2^53).
+    """
+    qx = unpack_nibbles(qx_packed).astype(F64)
+    qw = unpack_nibbles(wq_packed).astype(F64)
+    M, K = qx.shape
+    N = qw.shape[0]
+    G = K // GROUP
+    P = np.empty((M, N, G), dtype=np.int32)
+    for g in range(G):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        P[:, :, g] = (qx[:, sl] @ qw[:, sl].T).astype(np.int32)
+    return P
+
+
+def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
+    """Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 + b in float64.
+
+    [Term] 2.3 (E4) and (E7); bias added once.  The low-bit term is
+    sum_g sx[m, g] * sw[n, g] * P[m, n, g] with exact integer P.
+    Returns float64 [M, N].
+    """
+    qx, sx, T, _ = quantize_activations(X_bf16, s, L1_bf16)
+    qxv = unpack_nibbles(qx).astype(F64)
+    qwv = unpack_nibbles(Wq).astype(F64)
+    sw = np.asarray(w_scales, dtype=F32).astype(F64)
+    sxd = sx.astype(F64)
+    M, K = qxv.shape
+    N = qwv.shape[0]
+    main = np.zeros((M, N), dtype=F64)
+    for g in range(K // GROUP):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        Pg = qxv[:, sl] @ qwv[:, sl].T
+        main += (sxd[:, g][:, None] * sw[:, g][None, :]) * Pg
+    if T.shape[1] > 0:
+        low = T @ bf16_to_f64(L2_bf16)
+    else:
+        low = np.zeros((M, N), dtype=F64)
+    Y = main + low
+    if bias_bf16 is not None:
+        Y = Y + bf16_to_f64(bias_bf16)[None, :]
+    return Y
+
+
+def forward_exact(X_bf16, W, bias_bf16=None):
+    """Unquantized reference X W^T + b in float64 (what E4 approximates)."""
+    Y = bf16_to_f64(X_bf16) @ np.asarray(W, dtype=F32).astype(F64).T
+    if bias_bf16 is not None:
+        Y = Y + bf16_to_f64(bias_bf16)[None, :]
+    return Y
+
+
+# --------------------------------------------------------- comparisons
+def rel_fro(Y, Yref) -> float:
+    Y = np.asarray(Y, dtype=F64)
+    Yref = np.asarray(Yref, dtype=F64)
+    return float(np.linalg.norm(Y - Yref) / max(np.linalg.norm(Yref), 1e-300))
+
+
+def max_abs_ratio(Y, Yref) -> float:
+    Y = np.asarray(Y, dtype=F64)
+    Yref = np.asarray(Yref, dtype=F64)
+    return float(np.max(np.abs(Y - Yref)) / max(np.max(np.abs(Yref)), 1e-300))

@@ -1,0 +1,382 @@
+"""Pins for the CPU oracle, each one fixed by the pages or by mathematics, not by
+re-typing the oracle's own formulas.
+
+Citations: [Term] = the "SVDQuant Low-Rank Residual Quantization Algorithm
+Terminology Entry", section 2.3 (equations E1-E7 as numbered in the oracle's
+header); [Abs] = the SVDQuant abstract page.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svdq_oracle as O
+import synth
+
+F32, F64 = np.float32, np.float64
+
+
+def _bits(x):
+    return np.asarray(x, dtype=F32).view(np.uint32)
+
+
+# ------------------------------------------------------------ bfloat16 helper
+def test_bf16_matches_torch_on_float32_inputs():
+    g = np.random.Generator(np.random.PCG64(1))
+    x = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000),
+                        np.array([0.0, -0.0, 1.00390625, 1.01171875, 3.0e38, 1e-40, -1e-41])]).astype(F32)
+    ours = O.bf16_from_f64(x.astype(F64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_bf16_rounds_float64_once():
+    # 1 + 2^-8 + 2^-40 lies above the tie: one rounding gives 1 + 2^-7.
+    # (Rounding to float32 first would land on the tie and then go to 1.0.)
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert O.bf16_to_f64(O.bf16_from_f64(np.array([v])))[0] == 1.0 + 2.0 ** -7
+    # exact ties go to even
+    assert O.bf16_to_f64(O.bf16_from_f64(np.array([1.0 + 2.0 ** -8])))[0] == 1.0
+    assert O.bf16_to_f64(O.bf16_from_f64(np.array([1.0 + 3 * 2.0 ** -8])))[0] == 1.0 + 2.0 ** -6
+
+
+# -------------------------------------------------------------- stage one (E1, E2)
+def test_act_and_weight_absmax_by_hand():
+    X = synth.f32_to_bf16_bits(np.array([[1.0, -3.0, 0.5], [-2.0, 2.0, -0.25]], dtype=F32))
+    np.testing.assert_array_equal(O.act_absmax(X), np.array([2.0, 3.0, 0.5], dtype=F32))
+    W = np.array([[0.5, -4.0], [-1.5, 1.0], [1.0, 0.25]], dtype=F32)  # [N=3, K=2]
+    np.testing.assert_array_equal(O.weight_absmax(W), np.array([1.5, 4.0], dtype=F32))
+
+
+def test_smoothing_closed_forms():
+    A = np.array([4.0, 9.0, 0.5, 0.0], dtype=F32)
+    Wsc = np.array([0.25, 0.5, 2.0, 0.0], dtype=F32)
+    # alpha = 1: s = A (floored statistics)
+    np.testing.assert_array_equal(O.smoothing_factors(A, Wsc, 1.0), np.array([4.0, 9.0, 0.5, 1e-5], dtype=F32))
+    # alpha = 0: s = 1 / W_scale
+    np.testing.assert_array_equal(O.smoothing_factors(A, Wsc, 0.0),
+                                  np.array([4.0, 2.0, 0.5, 1e5], dtype=F32))
+    # alpha = 1/2: s = sqrt(A / W_scale); A = 4, W_scale = 1/4 gives 4 exactly
+    s = O.smoothing_factors(A, Wsc, 0.5)
+    assert s[0] == 4.0 and s[2] == 0.5 and s[3] == 1.0
+    assert abs(float(s[1]) - math.sqrt(9.0) / math.sqrt(0.5)) < 1e-6 * 4.3
+    # s_min holds
+    assert O.smoothing_factors(np.array([1e-9], F32), np.array([10.0], F32), 0.5, s_min=1e-2)[0] == F32(1e-2)
+
+
+def test_smoothing_is_an_identity_E1():
+    w = synth.WORKLOADS["tiny"]
+    X = synth.activations(w)[:64]
+    W = synth.weight(w)[:96]                      # N != K catches a transposed scaling
+    s = O.smoothing_factors(O.act_absmax(X), O.weight_absmax(W), 0.5)
+    ref = O.bf16_to_f64(X) @ W.astype(F64).T
+    exact = (O.bf16_to_f64(X) / s.astype(F64)[None, :]) @ O.smooth_weight(W, s).T
+    assert O.rel_fro(exact, ref) < 1e-13
+    # the float32 smoothed activations the method quantizes keep the identity to float32 accuracy
+    fl = O.smooth_activations(X, s).astype(F64) @ O.smooth_weight(W, s).T
+    assert O.rel_fro(fl, ref) < 1e-6
+
+
+# --------------------------------------------------------- stage two (E3, E5, E6)
+def test_svd_special_cases():
+    d = np.array([0.5, -3.0, 2.0, 0.0, 1.0])
+    U, S, V = O.svd_sorted(np.diag(d))
+    np.testing.assert_allclose(S, [3.0, 2.0, 1.0, 0.5, 0.0], atol=1e-15)
+    u = np.array([1.0, 2.0, -2.0])
+    v = np.array([3.0, 0.0, 4.0, 0.0])
+    _, S, _ = O.svd_sorted(np.outer(u, v))
+    assert abs(S[0] - 15.0) < 1e-13 and np.all(np.abs(S[1:]) < 1e-13)
+    # 2x2 closed form: singular values of [[a, b], [0, c]]
+    a, b, c = 3.0, 4.0, 2.0
+    tr = a * a + b * b + c * c
+    det = (a * c) ** 2
+    s1 = math.sqrt((tr + math.sqrt(tr * tr - 4 * det)) / 2)
+    s2 = math.sqrt((tr - math.sqrt(tr * tr - 4 * det)) / 2)
+    _, S, _ = O.svd_sorted(np.array([[a, b], [0.0, c]]))
+    np.testing.assert_allclose(S, [s1, s2], rtol=1e-14)
+
+
+def test_svd_recovers_a_pure_spike():
+    w = synth.WORKLOADS["tiny"]
+    g = synth.rng_for("tiny", 1)
+    U0, _ = np.linalg.qr(g.standard_normal((300, 8)))
+    V0, _ = np.linalg.qr(g.standard_normal((200, 8)))
+    sig = np.linspace(5, 1, 8)
+    U, S, V = O.svd_sorted((U0 * sig) @ V0.T)
+    np.testing.assert_allclose(S[:8], sig, rtol=1e-12)
+    assert np.all(S[8:] < 1e-12)
+    # sign convention: the largest-magnitude entry of each v_i is positive
+    idx = np.argmax(np.abs(V[:, :8]), axis=0)
+    assert np.all(V[idx, np.arange(8)] > 0)
+
+
+@pytest.mark.parametrize("r", [0, 4, 16])
+def test_eckart_young_and_orthogonality_E5_E6(r):
+    w = synth.WORKLOADS["tiny"]
+    W = synth.weight(w)[:160, :192]
+    s = O.smoothing_factors(np.ones(192, F32), O.weight_absmax(W), 0.5)
+    What = O.smooth_weight(W, s)
+    U, S, V = O.svd_sorted(What)
+    assert np.all(np.diff(S) <= 0)
+    p = S.shape[0]
+    np.testing.assert_allclose(U.T @ U, np.eye(p), atol=1e-12)
+    np.testing.assert_allclose(V.T @ V, np.eye(p), atol=1e-12)
+    fro2 = float(np.sum(What ** 2))
+    assert abs(fro2 - float(np.sum(S ** 2))) < 1e-12 * fro2
+    L = (U[:, :r] * S[:r]) @ V[:, :r].T
+    tail = float(np.sum(S[r:] ** 2))
+    assert abs(float(np.sum((What - L) ** 2)) - tail) < 1e-10 * fro2
+    # optimality: random rank-r competitors built from perturbed subspaces do worse
+    g = synth.rng_for("tiny", 2)
+    for _ in range(3):
+        if r == 0:
+            break
+        Q, _ = np.linalg.qr(V[:, :r] + 0.05 * g.standard_normal((192, r)))
+        Lc = (What @ Q) @ Q.T                    # best approximation within that row space
+        assert float(np.sum((What - Lc) ** 2)) > tail
+
+
+def test_lowrank_factors_put_sigma_on_lora_up():
+    w = synth.WORKLOADS["tiny"]
+    W = synth.weight(w)[:128, :256]
+    U, S, V = O.svd_sorted(W.astype(F64))
+    L1, L2 = O.lowrank_factors(U, S, V, 8)
+    assert L1.shape == (256, 8) and L2.shape == (8, 128)
+    # lora_down columns are unit vectors (to bfloat16 accuracy); lora_up rows carry sigma
+    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L1), axis=0), 1.0, rtol=1e-2)
+    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L2), axis=1), S[:8], rtol=1e-2)
+    # (L1 L2)^T approximates W_r with the tail energy (E6) up to bfloat16 rounding
+    Lr = (O.bf16_to_f64(L1) @ O.bf16_to_f64(L2)).T
+    err2 = float(np.sum((W.astype(F64) - Lr) ** 2))
+    assert abs(err2 - float(np.sum(S[8:] ** 2))) < 2e-2 * float(np.sum(S[:8] ** 2)) ** 0.5 * 2 ** -6
+
+
+def test_residual_of_an_exact_lowrank_weight_is_zero():
+    """W_hat = (L1 L2)^T exactly (dyadic factors, N != K): R = W_hat - L1 L2 must be exactly 0."""
+    g = synth.rng_for("tiny", 3)
+    K, N, r = 192, 128, 5
+    L1v = g.integers(-16, 17, (K, r)) / 16.0
+    L2v = g.integers(-16, 17, (r, N)) / 8.0
+    L1 = O.bf16_from_f64(L1v)
+    L2 = O.bf16_from_f64(L2v)
+    What = (L1v @ L2v).T
+    R = O.residual(What, L1, L2)
+    assert R.dtype == F32 and np.all(R == 0)
+    q, sc = O.quantize_groups(R, weight_scale=True)
+    assert np.all(q == 0) and np.all(sc == 0)
+    # and a non-zero remainder survives exactly where it was put
+    What2 = What.copy()
+    What2[3, 70] += 0.75
+    R2 = O.residual(What2, L1, L2)
+    assert R2[3, 70] == F32(0.75) and np.count_nonzero(R2) == 1
+
+
+# -------------------------------------------------------------------- Q (E4)
+def test_quantizer_ties_go_to_even_by_hand():
+    v = np.zeros(64, F32)
+    v[:8] = [7.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -7.0]
+    q, sc = O.quantize_groups(v[None, :])
+    assert sc[0, 0] == 1.0
+    np.testing.assert_array_equal(q[0, :8], [7, 2, 4, -2, 0, 2, 0, -7])
+    # a = 3.5: scale = 0.5, inv = 2 -> 1.25 * 2 = 2.5 -> 2, 1.75 * 2 = 3.5 -> 4
+    v = np.zeros(64, F32)
+    v[:3] = [3.5, 1.25, -1.75]
+    q, sc = O.quantize_groups(v[None, :])
+    assert sc[0, 0] == 0.5
+    np.testing.assert_array_equal(q[0, :3], [7, 2, -4])
+
+
+def test_quantizer_zero_group_and_absmax_code():
+    v = np.zeros((2, 128), F32)
+    v[1, 64:] = np.linspace(-0.3, 0.9, 64, dtype=F32)
+    q, sc = O.quantize_groups(v)
+    assert sc[0, 0] == 0 and sc[0, 1] == 0 and sc[1, 0] == 0 and np.all(q[0] == 0)
+    assert q[1, 127] == 7 and sc[1, 1] == F32(F32(0.9) / F32(7))
+
+
+def test_quantizer_error_bound_and_range():
+    g = synth.rng_for("tiny", 4)
+    v = (g.standard_normal((64, 1024)) * np.exp(g.uniform(-8, 8, (64, 1)))).astype(F32)
+    for wscale in (False, True):
+        q, sc = O.quantize_groups(v, weight_scale=wscale)
+        assert q.min() >= -7 and q.max() <= 7
+        deq = q.reshape(64, 16, 64).astype(F64) * sc.astype(F64)[..., None]
+        err = np.abs(v.reshape(64, 16, 64).astype(F64) - deq)
+        assert np.all(err <= sc.astype(F64)[..., None] / 2 * (1 + 2.0 ** -16) + 1e-300)
+        # the group's absmax element maps to +-7
+        amax_idx = np.argmax(np.abs(v.reshape(64, 16, 64)), axis=-1)
+        got = np.take_along_axis(np.abs(q.reshape(64, 16, 64)), amax_idx[..., None], -1)
+        assert np.all(got == 7)
+    # weight scales have the two low significand bits clear, so 3 * scale is exact in float32
+    assert np.all((_bits(sc) & 3) == 0)
+    assert np.all((F32(3) * sc).astype(F64) == 3.0 * sc.astype(F64))
+
+
+def test_quantizer_power_of_two_equivariance():
+    g = synth.rng_for("tiny", 5)
+    v = g.standard_normal((8, 256)).astype(F32)
+    q0, s0 = O.quantize_groups(v)
+    for k in (-5, 3, 11):
+        q1, s1 = O.quantize_groups((v * F32(2.0 ** k)).astype(F32))
+        np.testing.assert_array_equal(q1, q0)
+        np.testing.assert_array_equal(s1, s0 * F32(2.0 ** k))
+
+
+def test_nibble_packing_by_hand():
+    q = np.array([[1, -1, 7, -7, 0, 3] + [0] * 58], dtype=np.int8)
+    b = O.pack_nibbles(q)
+    assert b.shape == (1, 32)
+    assert list(b[0, :3]) == [0xF1, 0x97, 0x30]
+    np.testing.assert_array_equal(O.unpack_nibbles(b), q)
+
+
+def test_group_partials_brute_force():
+    g = synth.rng_for("tiny", 6)
+    qx = g.integers(-7, 8, (3, 128)).astype(np.int8)
+    qw = g.integers(-7, 8, (5, 128)).astype(np.int8)
+    P = O.group_partials(O.pack_nibbles(qx), O.pack_nibbles(qw))
+    assert P.shape == (3, 5, 2)
+    for m in range(3):
+        for n in range(5):
+            for gg in range(2):
+                acc = 0
+                for k in range(64 * gg, 64 * gg + 64):
+                    acc += int(qx[m, k]) * int(qw[n, k])
+                assert P[m, n, gg] == acc
+    # extreme codes: |P| reaches 64 * 49
+    P = O.group_partials(O.pack_nibbles(np.full((1, 64), -7, np.int8)), O.pack_nibbles(np.full((1, 64), 7, np.int8)))
+    assert P[0, 0, 0] == -3136
+
+
+# --------------------------------------------------------------- forward (E4, E7)
+def _lossless_problem(M=6, K=128, N=96, r=3, seed=7):
+    """Inputs on which both quantizers are lossless, so E4 holds with equality:
+    Y must equal X W^T + b up to float64 rounding."""
+    g = synth.rng_for("tiny", seed)
+    G = K // 64
+    s = (2.0 ** g.integers(-2, 3, K)).astype(F32)
+    # activations: x_hat = q * 2^e with each group's absmax code = 7
+    qx = g.integers(-7, 8, (M, K))
+    qx[:, ::64] = 7 * np.where(g.random((M, G)) < 0.5, 1, -1)
+    ex = 2.0 ** g.integers(-3, 2, (M, G))
+    xh = qx * np.repeat(ex, 64, axis=1)
+    X = synth.f32_to_bf16_bits((xh * s[None, :]).astype(F32))
+    assert np.all(O.bf16_to_f64(X) == xh * s[None, :])
+    # residual: R = q * 2^f with each group's absmax code = 7
+    qr = g.integers(-7, 8, (N, K))
+    qr[:, 5::64] = 7
+    ew = 2.0 ** g.integers(-6, -2, (N, G))
+    R = qr * np.repeat(ew, 64, axis=1)
+    L1v = g.integers(-8, 9, (K, r)) / 8.0
+    L2v = g.integers(-8, 9, (r, N)) / 16.0
+    What = R + (L1v @ L2v).T
+    W = (What / s[None, :].astype(F64)).astype(F32)
+    assert np.all(W.astype(F64) * s[None, :] == What)
+    b = synth.f32_to_bf16_bits(g.standard_normal(N).astype(F32))
+    return X, W, s, O.bf16_from_f64(L1v), O.bf16_from_f64(L2v), b
+
+
+def test_forward_equals_xw_plus_b_when_quantization_is_lossless():
+    X, W, s, L1, L2, b = _lossless_problem()
+    Wq, ws = O.quantize_residual(W, s, L1, L2)
+    Y = O.forward(X, s, L1, L2, Wq, ws, b)
+    Yx = O.forward_exact(X, W, b)
+    assert O.rel_fro(Y, Yx) < 1e-14
+    # dropping either branch or the bias breaks it
+    Y0 = O.forward(X, s, np.zeros((W.shape[1], 0), np.uint16), np.zeros((0, W.shape[0]), np.uint16), Wq, ws, b)
+    assert O.rel_fro(Y0, Yx) > 1e-3
+    assert O.rel_fro(O.forward(X, s, L1, L2, Wq, ws, None), Yx) > 1e-3
+
+
+def test_rank_zero_collapses_to_plain_w4a4():
+    w = synth.WORKLOADS["tiny"]
+    X = synth.activations(w)[:32]
+    W = synth.weight(w)[:80]
+    b = synth.bias(w)[:80]
+    A = O.act_absmax(synth.calibration_activations(w))
+    pk = O.pack_weights(W, A, 0.5, rank=0)
+    assert np.all(pk["R"] == pk["What"].astype(F32))
+    Y = O.forward(X, pk["s"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+    # independent route: dequantize both operands, one float64 matrix product
+    qx, sx, _, _ = O.quantize_activations(X, pk["s"])
+    dx = O.unpack_nibbles(qx).astype(F64) * np.repeat(sx.astype(F64), 64, axis=1)
+    dw = O.unpack_nibbles(pk["Wq"]).astype(F64) * np.repeat(pk["w_scales"].astype(F64), 64, axis=1)
+    Yd = dx @ dw.T + O.bf16_to_f64(b)[None, :]
+    assert O.rel_fro(Y, Yd) < 1e-13
+    # s = 1 gives the naive W4A4 of the unsmoothed operands
+    pk1 = O.pack_weights(W, O.weight_absmax(W), 0.5, rank=0)
+    assert np.all(pk1["s"] == 1.0)
+
+
+def test_svdquant_beats_smoothing_alone_beats_naive():
+    """[Abs]: smoothing alone is insufficient at 4 bits; the low-rank branch absorbs the outliers."""
+    w = synth.WORKLOADS["tiny"]
+    X = synth.activations(w)
+    W = synth.weight(w)
+    b = synth.bias(w)
+    A = O.act_absmax(synth.calibration_activations(w))
+    Yx = O.forward_exact(X, W, b)
+    errs = {}
+    for name, AA, r in (("svdq", A, 16), ("smooth", A, 0), ("naive", O.weight_absmax(W), 0)):
+        pk = O.pack_weights(W, AA, 0.5, rank=r)
+        Y = O.forward(X, pk["s"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+        errs[name] = O.rel_fro(Y, Yx)
+    assert errs["svdq"] < errs["smooth"] < errs["naive"], errs
+
+
+def test_activation_codes_power_of_two_equivariance():
+    w = synth.WORKLOADS["tiny"]
+    X = synth.activations(w)[:16]
+    s = O.smoothing_factors(O.act_absmax(X), np.full(w.K, 0.1, F32), 0.5)
+    qx0, sx0, _, _ = O.quantize_activations(X, s)
+    X4 = synth.f32_to_bf16_bits(O.bf16_to_f32(X) * F32(4))
+    qx1, sx1, _, _ = O.quantize_activations(X4, s)
+    np.testing.assert_array_equal(qx1, qx0)
+    np.testing.assert_array_equal(sx1, sx0 * F32(4))
+
+
+def test_quantizer_matches_exact_rational_evaluation():
+    """Each rounding point of Q evaluated with exact rationals and one IEEE rounding each."""
+    g = synth.rng_for("tiny", 8)
+    v = (g.standard_normal(64) * 3).astype(F32)
+
+    def rn32(fr):                      # round a Fraction to the nearest float32 (ties to even)
+        f = F32(float(fr))             # float(Fraction) is correctly rounded to float64
+        lo, hi = sorted([f, np.nextafter(f, F32(np.inf) if Fraction(float(f)) < fr else F32(-np.inf))])
+        dlo, dhi = abs(Fraction(float(lo)) - fr), abs(Fraction(float(hi)) - fr)
+        if dlo != dhi:
+            return lo if dlo < dhi else hi
+        return lo if (_bits(lo) & 1) == 0 else hi
+
+    a = max(abs(Fraction(float(x))) for x in v)
+    scale = rn32(a / 7)
+    inv = rn32(7 / a)
+    want = []
+    for x in v:
+        t = Fraction(float(rn32(Fraction(float(x)) * Fraction(float(inv)))))
+        fl = math.floor(t)
+        d = t - fl
+        qi = fl + (1 if d > Fraction(1, 2) or (d == Fraction(1, 2) and fl % 2 == 1) else 0)
+        want.append(max(-7, min(7, qi)))
+    q, sc = O.quantize_groups(v[None, :])
+    assert sc[0, 0] == scale
+    np.testing.assert_array_equal(q[0], np.array(want, np.int8))
+
+
+def test_quantizer_golden_examples():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "quantizer_examples.txt")
+    n = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        vals, scale, codes = [p.split() for p in line.split("|")]
+        v = np.zeros(64, F32)
+        v[:len(vals)] = [float(t) for t in vals]
+        q, sc = O.quantize_groups(v[None, :])
+        assert sc[0, 0] == F32(float(scale[0]))
+        np.testing.assert_array_equal(q[0, :len(codes)], [int(c) for c in codes])
+        n += 1
+    assert n == 4
