@@ -1,0 +1,156 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant W4A4 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes (SVDQuant Terminology Entry, section 2.3, equation E4,
+ * with the bias of its right-hand side):
+ *
+ *     Y = Q(X diag(s)^-1) Q(R)  +  (X diag(s)^-1 L1^T) L2^T  +  b,
+ *     R = diag(s) W - (L1^T L2^T)^T   i.e.  R[n,k] = W[n,k] s[k] - sum_j L2[n,j] L1[j,k]
+ *
+ * where s smooths activation outliers into the weight (E1, E2), L1 and L2 are
+ * the rank-r truncated SVD factors of the smoothed weight (E3, E5) kept in
+ * bfloat16, and Q is symmetric 4-bit quantization with one float32 scale per
+ * 64 consecutive input channels (the SVDQuant abstract fixes 4-bit weights and
+ * activations; the group size and scale format are this library's reading).
+ *
+ * Storage conventions (all row-major, little-endian):
+ *   bf16        uint16_t bit patterns of bfloat16
+ *   W           float32 [N, K]      out-features x in-features
+ *   X           bf16    [M, K]      M tokens
+ *   s (smooth)  float32 [K]
+ *   L1          bf16    [r, K]      lora_down, row j = v_j^T          (V_r^T)
+ *   L2          bf16    [N, r]      lora_up,   row n = (U_r Sigma_r)[n, :]
+ *   Wq          uint8   [N, K/2]    two int4 codes per byte, even k in the low nibble
+ *   w_scales    float32 [N, K/64]   two lowest significand bits always zero
+ *   qx          uint8   [M, K/2]    activation codes, same packing
+ *   sx          float32 [M, K/64]   activation scales
+ *   T           float32 [M, r]      lora_down output  x_hat L1^T
+ *   bias        bf16    [N]         may be NULL (zero bias)
+ *   Y           bf16    [M, N]
+ * Codes are in [-7, 7]; -8 is never produced.
+ *
+ * Quantization of one group v[0..63] (float32):
+ *   a = max|v|; a == 0 -> scale 0, codes 0; else scale = fl32(a / 7),
+ *   inv = fl32(7 / a), code = clamp(round_half_even(fl32(v * inv)), -7, 7).
+ *   A weight scale then has its two lowest significand bits cleared.
+ * Smoothed activations: x_hat[m,k] = fl32(X[m,k] * fl32(1 / s[k])).
+ *
+ * Errors: every function returns an svdq_status and never throws or aborts.
+ * On a validation error nothing is written.  Device functions launch work
+ * asynchronously on the given stream (a hipStream_t; NULL = the null stream)
+ * and do not synchronize; SVDQ_ERR_HIP reports a launch failure.  Non-finite
+ * inputs are not checked: their results are undefined.  svdq_last_error()
+ * returns a thread-local description of the last failure on this thread.
+ *
+ * Ownership: the caller owns every buffer.  Host functions take host
+ * pointers; device functions take device pointers.  The library allocates no
+ * device memory; scratch space comes from the caller's workspace.
+ */
+#ifndef SVDQ_H_
+#define SVDQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = 1,    /* a size or pointer argument is out of range */
+  SVDQ_ERR_UNSUPPORTED = 2,    /* a parameter the library does not implement (e.g. group != 64) */
+  SVDQ_ERR_ALIGNMENT = 3,      /* a device pointer is not 16-byte aligned */
+  SVDQ_ERR_WORKSPACE = 4,      /* workspace_bytes below svdq_forward_workspace_bytes() */
+  SVDQ_ERR_NO_CONVERGENCE = 5, /* the packer's eigensolver did not converge */
+  SVDQ_ERR_HIP = 6             /* a HIP runtime call failed */
+} svdq_status;
+
+typedef struct {
+  float alpha;  /* migration strength of E2, in [0, 1] */
+  int rank;     /* r: 0 <= r <= 128, r % 16 == 0 (the page recommends r <= 128) */
+  int group;    /* quantization group along K; must be 64 */
+  float s_min;  /* lower bound of s (E2); both statistics are floored at 1e-5 */
+} svdq_pack_params;
+
+/* ------------------------------------------------------------------ host */
+
+/* Calibration statistic A_scale of E2 (Terminology Entry, section 2.3: the
+ * per-channel absolute maximum of the activations).  Folds M rows of bf16
+ * activations X [M, K] into the running maximum amax [K]:
+ * amax[k] = max(amax[k], max_m |X[m,k]|).  Start from zeros.  Host memory. */
+svdq_status svdq_act_absmax_update(const uint16_t* X, int64_t M, int K, float* amax);
+
+/* Offline packing: the three stages of the Terminology Entry, section 2.1, in
+ * order.  (1) s[k] = max(max(A,1e-5)^alpha / max(Wsc,1e-5)^(1-alpha), s_min) in
+ * float64, stored float32 (E2), with Wsc[k] = max_n |W[n,k]|.  (2) the rank-r
+ * truncated SVD of W_hat = W diag(s) (E3, E5); L1 = bf16(V_r^T),
+ * L2 = bf16(U_r Sigma_r), each rounded once from float64; the sign of each
+ * singular pair is chosen so that the largest-magnitude entry of v_j is
+ * positive.  (3) R = fl32(W_hat - L2 L1) from the rounded factors (the sum
+ * over j ascending in float64), quantized per 64-group into Wq and w_scales.
+ * Host buffers, sizes as in the storage table; sigma (optional, may be NULL)
+ * receives the min(N,K) singular values of W_hat in descending order.  r = 0
+ * writes nothing to L1/L2 (they may be NULL).  Requires K % 64 == 0, N >= 1.
+ * Returns SVDQ_ERR_NO_CONVERGENCE if the eigensolver fails. */
+svdq_status svdq_pack_weights(const float* W, int N, int K, const float* act_absmax,
+                              const svdq_pack_params* params, float* smooth, uint16_t* L1,
+                              uint16_t* L2, uint8_t* Wq, float* w_scales, double* sigma);
+
+/* Stage (3) alone: Wq and w_scales from given s, L1, L2 (host memory).
+ * Bit-exact contract: the same inputs always give the same bytes. */
+svdq_status svdq_quantize_residual(const float* W, int N, int K, const float* smooth,
+                                   const uint16_t* L1, const uint16_t* L2, int r, uint8_t* Wq,
+                                   float* w_scales);
+
+/* ---------------------------------------------------------------- device */
+
+/* Workspace the forward needs: qx, sx and T, each part 256-byte aligned. */
+size_t svdq_forward_workspace_bytes(int M, int K, int r);
+
+/* The SVDQuant linear forward (E4): launches the fused smooth + quantize +
+ * lora_down kernel, then the W4A4 GEMM whose epilogue applies the group
+ * scales, adds the lora_up product and the bias and stores bf16 Y.
+ * Requires M >= 1, K % 64 == 0, N % 16 == 0, 0 <= r <= 128, r % 16 == 0,
+ * 16-byte aligned device pointers (bias and, for r = 0, L1/L2 may be NULL)
+ * and workspace_bytes >= svdq_forward_workspace_bytes(M, K, r).  Asynchronous
+ * on `stream`; no allocation, no synchronization. */
+svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
+                                const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                const uint8_t* Wq, const float* w_scales, const uint16_t* bias,
+                                uint16_t* Y, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* The two halves of svdq_linear_forward, for callers that schedule or time
+ * them separately.  Stage 1 writes qx, sx, T into the workspace; stage 2
+ * reads them and writes Y.  Same requirements as svdq_linear_forward. */
+svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const float* smooth,
+                                  const uint16_t* L1, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                              const float* w_scales, const uint16_t* bias, uint16_t* Y,
+                              const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 into caller buffers in the canonical layouts: Q(X diag(s)^-1) as
+ * qx [M, K/2] and sx [M, K/64], and T = x_hat L1^T [M, r] in float32
+ * (T may be NULL when r == 0).  Device memory, asynchronous. */
+svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const float* smooth,
+                                      const uint16_t* L1, int r, uint8_t* qx, float* sx,
+                                      float* T, void* stream);
+
+/* The integer group partial sums of Q(x_hat) Q(R) (E4, E7) over the output
+ * block rows [m0, m1) x columns [n0, n1), computed by the same MFMA main loop
+ * the forward runs: P[(m-m0), (n-n0), g] = sum_{k in group g} qx[m,k] qw[n,k],
+ * int32 [(m1-m0), (n1-n0), K/64].  Requires 0 <= m0 < m1 <= M,
+ * 0 <= n0 < n1 <= N, N % 16 == 0, K % 64 == 0.  Device memory, asynchronous. */
+svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
+                                      int m0, int m1, int n0, int n1, int32_t* P, void* stream);
+
+const char* svdq_status_string(svdq_status status);
+const char* svdq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H_ */

@@ -29,8 +29,10 @@ design notes):
   weights are stored [N, K] (out, in) and s indexes input channels k;
   W_scale is the per-input-channel absolute maximum;
   s_min = 1e-5 and both statistics are floored at 1e-5 before the power;
-  the low-rank factors are L1 = V_r (lora_down, [K, r]) and
-  L2 = (U_r Sigma_r)^T (lora_up, [r, N]), both rounded to bfloat16;
+  the low-rank factors are L1 = V_r^T (lora_down, stored [r, K]) and
+  L2 = U_r Sigma_r (lora_up, stored [N, r]), both rounded to bfloat16 --
+  the page's V [in, rank] and (U S)^T [rank, out] kept in the same
+  [out, in] storage order as W;
   R is formed from the rounded factors;
   Q is symmetric 4-bit, one float32 scale per 64 consecutive input channels,
   scale = fl32(amax / 7), codes = clamp(rne(fl32(v * fl32(7 / amax))), -7, 7),
@@ -166,18 +168,18 @@ def svd_sorted(What):
 
 
 def lowrank_factors(U, S, V, r: int):
-    """L1 = bf16(V_r) [K, r] (lora_down), L2 = bf16((U_r Sigma_r)^T) [r, N] (lora_up).
+    """L1 = bf16(V_r^T) stored [r, K] (lora_down), L2 = bf16(U_r Sigma_r) stored [N, r] (lora_up).
 
     [Term] 2.3 (E4): the branch is (X diag(s)^-1 V)(U S)^T, so Sigma rides
     with U.  Returns uint16 bfloat16 bit patterns.
     """
-    L1 = bf16_from_f64(V[:, :r])
-    L2 = bf16_from_f64((U[:, :r] * S[None, :r]).T)
+    L1 = bf16_from_f64(V[:, :r].T)
+    L2 = bf16_from_f64(U[:, :r] * S[None, :r])
     return L1, L2
 
 
 def residual(What, L1_bf16, L2_bf16) -> np.ndarray:
-    """R = fl32(W_hat - L1 L2) with R[n, k] = W_hat[n, k] - sum_j L1[k, j] L2[j, n].
+    """R = fl32(W_hat - (U S) V^T) with R[n, k] = W_hat[n, k] - sum_j L2[n, j] L1[j, k].
 
     [Term] 2.3 (E3) with the stored (rounded) factors.  The inner sum runs
     over j in ascending order in float64 starting from 0, each product exact
@@ -186,10 +188,10 @@ def residual(What, L1_bf16, L2_bf16) -> np.ndarray:
     What = np.asarray(What, dtype=F64)
     L1 = bf16_to_f64(L1_bf16)
     L2 = bf16_to_f64(L2_bf16)
-    r = L1.shape[1] if L1.ndim == 2 else 0
+    r = L1.shape[0] if L1.ndim == 2 else 0
     acc = np.zeros(What.shape, dtype=F64)
     for j in range(r):
-        acc += L2[j, :][:, None] * L1[:, j][None, :]
+        acc += L2[:, j][:, None] * L1[j, :][None, :]
     return (What - acc).astype(F32)
 
 
@@ -274,7 +276,7 @@ def smooth_activations(X_bf16, s) -> np.ndarray:
 
 
 def quantize_activations(X_bf16, s, L1_bf16=None):
-    """First half of (E4): Q(X diag(s)^-1) and the lora_down product T = x_hat L1.
+    """First half of (E4): Q(X diag(s)^-1) and the lora_down product T = x_hat L1^T.
 
     Returns (qx packed uint8 [M, K/2], sx float32 [M, K/64], T float64 [M, r], x_hat).
     """
@@ -283,7 +285,7 @@ def quantize_activations(X_bf16, s, L1_bf16=None):
     if L1_bf16 is None or np.asarray(L1_bf16).size == 0:
         T = np.zeros((xh.shape[0], 0), dtype=F64)
     else:
-        T = xh.astype(F64) @ bf16_to_f64(L1_bf16)
+        T = xh.astype(F64) @ bf16_to_f64(L1_bf16).T
     return pack_nibbles(q), sx, T, xh
 
 
@@ -307,7 +309,7 @@ def group_partials(qx_packed, wq_packed) -> np.ndarray:
 
 
 def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
-    """Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 + b in float64.
+    """Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1^T) L2^T + b in float64.
 
     [Term] 2.3 (E4) and (E7); bias added once.  The low-bit term is
     sum_g sx[m, g] * sw[n, g] * P[m, n, g] with exact integer P.
@@ -326,7 +328,7 @@ def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
         Pg = qxv[:, sl] @ qwv[:, sl].T
         main += (sxd[:, g][:, None] * sw[:, g][None, :]) * Pg
     if T.shape[1] > 0:
-        low = T @ bf16_to_f64(L2_bf16)
+        low = T @ bf16_to_f64(L2_bf16).T
     else:
         low = np.zeros((M, N), dtype=F64)
     Y = main + low

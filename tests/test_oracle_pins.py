@@ -143,25 +143,25 @@ def test_lowrank_factors_put_sigma_on_lora_up():
     W = synth.weight(w)[:128, :256]
     U, S, V = O.svd_sorted(W.astype(F64))
     L1, L2 = O.lowrank_factors(U, S, V, 8)
-    assert L1.shape == (256, 8) and L2.shape == (8, 128)
-    # lora_down columns are unit vectors (to bfloat16 accuracy); lora_up rows carry sigma
-    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L1), axis=0), 1.0, rtol=1e-2)
-    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L2), axis=1), S[:8], rtol=1e-2)
-    # (L1 L2)^T approximates W_r with the tail energy (E6) up to bfloat16 rounding
-    Lr = (O.bf16_to_f64(L1) @ O.bf16_to_f64(L2)).T
+    assert L1.shape == (8, 256) and L2.shape == (128, 8)
+    # lora_down rows are unit vectors (to bfloat16 accuracy); lora_up columns carry sigma
+    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L1), axis=1), 1.0, rtol=1e-2)
+    np.testing.assert_allclose(np.linalg.norm(O.bf16_to_f64(L2), axis=0), S[:8], rtol=1e-2)
+    # L2 L1 approximates W_r with the tail energy (E6) up to bfloat16 rounding
+    Lr = O.bf16_to_f64(L2) @ O.bf16_to_f64(L1)
     err2 = float(np.sum((W.astype(F64) - Lr) ** 2))
     assert abs(err2 - float(np.sum(S[8:] ** 2))) < 2e-2 * float(np.sum(S[:8] ** 2)) ** 0.5 * 2 ** -6
 
 
 def test_residual_of_an_exact_lowrank_weight_is_zero():
-    """W_hat = (L1 L2)^T exactly (dyadic factors, N != K): R = W_hat - L1 L2 must be exactly 0."""
+    """W_hat = L2 L1 exactly (dyadic factors, N != K): R = W_hat - L2 L1 must be exactly 0."""
     g = synth.rng_for("tiny", 3)
     K, N, r = 192, 128, 5
-    L1v = g.integers(-16, 17, (K, r)) / 16.0
-    L2v = g.integers(-16, 17, (r, N)) / 8.0
+    L1v = g.integers(-16, 17, (r, K)) / 16.0
+    L2v = g.integers(-16, 17, (N, r)) / 8.0
     L1 = O.bf16_from_f64(L1v)
     L2 = O.bf16_from_f64(L2v)
-    What = (L1v @ L2v).T
+    What = L2v @ L1v
     R = O.residual(What, L1, L2)
     assert R.dtype == F32 and np.all(R == 0)
     q, sc = O.quantize_groups(R, weight_scale=True)
@@ -269,9 +269,9 @@ def _lossless_problem(M=6, K=128, N=96, r=3, seed=7):
     qr[:, 5::64] = 7
     ew = 2.0 ** g.integers(-6, -2, (N, G))
     R = qr * np.repeat(ew, 64, axis=1)
-    L1v = g.integers(-8, 9, (K, r)) / 8.0
-    L2v = g.integers(-8, 9, (r, N)) / 16.0
-    What = R + (L1v @ L2v).T
+    L1v = g.integers(-8, 9, (r, K)) / 8.0
+    L2v = g.integers(-8, 9, (N, r)) / 16.0
+    What = R + L2v @ L1v
     W = (What / s[None, :].astype(F64)).astype(F32)
     assert np.all(W.astype(F64) * s[None, :] == What)
     b = synth.f32_to_bf16_bits(g.standard_normal(N).astype(F32))
@@ -285,7 +285,7 @@ def test_forward_equals_xw_plus_b_when_quantization_is_lossless():
     Yx = O.forward_exact(X, W, b)
     assert O.rel_fro(Y, Yx) < 1e-14
     # dropping either branch or the bias breaks it
-    Y0 = O.forward(X, s, np.zeros((W.shape[1], 0), np.uint16), np.zeros((0, W.shape[0]), np.uint16), Wq, ws, b)
+    Y0 = O.forward(X, s, np.zeros((0, W.shape[1]), np.uint16), np.zeros((W.shape[0], 0), np.uint16), Wq, ws, b)
     assert O.rel_fro(Y0, Yx) > 1e-3
     assert O.rel_fro(O.forward(X, s, L1, L2, Wq, ws, None), Yx) > 1e-3
 
