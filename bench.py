@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the SVDQuant W4A4 + low-rank linear on one MI355X.
+
+One step = one full forward of the layer over one batch of tokens: the fused
+smooth + quantize + lora_down kernel (k1), then the W4A4 GEMM with its scale
+epilogue, lora_up and bias (k2).  Inputs, packed weights and outputs rotate
+over more than 512 MB of buffers so that the 256 MB Infinity Cache cannot
+serve a step from the previous one.
+
+Prints one JSON line (rank 0).  Default workload: the DiT attention
+projection, M=4096 tokens, K=N=3072, rank 32.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dit_proj")
+    ap.add_argument("--rotate-mb", type=int, default=640, help="total bytes of rotated buffers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "bit_diffusion_model_svdq_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(workload, {}).get(kernel_file)
+        if e and e.get("source_sha256_16") == kernel_source_hash(kernel_file):
+            return e["bytes_per_launch"]
+    except Exception:
+        return None
+    return None
+
+
+def copy_probe():
+    import torch
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe:
+        copy_probe()
+        return
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import bit_diffusion_model_svdq_amd as S
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    M, K, N, r = w.M, w.K, w.N, w.rank
+    dev = torch.device("cuda:0")
+
+    # ---- offline pack (host, untimed) through the library's packer
+    t0 = time.time()
+    X = synth.activations(w)
+    W = synth.weight(w)
+    b = synth.bias(w)
+    A = np.zeros(K, np.float32)
+    S.svdq_act_absmax_update(synth.calibration_activations(w), A)
+    pk = S.svdq_pack_weights(W, A, w.alpha, r)
+    pack_s = time.time() - t0
+    print(f"# packed {args.workload} in {pack_s:.1f}s", file=sys.stderr, flush=True)
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    per_set = (M * K * 2 + M * N * 2 + S.svdq_forward_workspace_bytes(M, K, r)
+               + N * K // 2 + N * K // 64 * 4 + r * (K + N) * 2 + K * 4 + N * 2)
+    nsets = max(2, -(-args.rotate_mb * (1 << 20) // per_set))
+    sets = []
+    base = dict(X=t(X), s=t(pk["smooth"]), L1=t(pk["L1"]), L2=t(pk["L2"]), Wq=t(pk["Wq"]),
+                ws=t(pk["w_scales"]), b=t(b))
+    for i in range(nsets):
+        d = {k: v.clone() for k, v in base.items()}
+        d["Y"] = torch.empty((M, N), dtype=torch.int16, device=dev)
+        d["work"] = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
+        sets.append(d)
+    torch.cuda.synchronize()
+
+    def step(d):
+        S.svdq_forward_quantize(d["X"], d["s"], d["L1"], d["work"])
+        S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events on the launch stream around each kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        d = sets[i % nsets]
+        e = ev[i]
+        e[0].record()
+        S.svdq_forward_quantize(d["X"], d["s"], d["L1"], d["work"])
+        e[1].record()
+        S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+        e[2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_step = total_ms / args.steps
+
+    ops_main = 2.0 * M * N * K                 # int8 MFMA work of the W4A4 product
+    ops_low = 2.0 * M * r * (K + N)            # bf16 low-rank branch
+    tops = (ops_main + ops_low) / (ms_step * 1e-3) / 1e12
+    tokens_s = M / (ms_step * 1e-3)
+    k1_bytes = M * (2 * K + K // 2 + 4 * (K // 64) + 4 * r) + r * K * 2 + K * 4
+    k2_achieved = ops_main / (k2_ms * 1e-3) / 1e12
+    k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "fused W4A4+low-rank linear TOPS and tokens/s at M=4096,K=N=3072,r=32 (% MFMA peak)",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "group": 64,
+                   "rotated_sets": nsets},
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_int8_mfma_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "roofline": {
+            "kernel": "w4a4_gemm (k2)",
+            "bound": "mfma",
+            "achieved": round(k2_achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(k2_achieved / PEAK_INT8_TOPS, 4),
+            "traffic": load_traffic("k2_w4a4_gemm.hip", args.workload),
+            "avg_launch_us": round(k2_ms * 1e3, 3),
+        },
+        "kernels": {
+            "k1_smooth_quant_lora_down": {"avg_launch_us": round(k1_ms * 1e3, 3), "bound": "hbm",
+                                          "algorithmic_bytes": k1_bytes, "achieved_GBs": round(k1_gbs, 1),
+                                          "peak_GBs": PEAK_HBM_GBS, "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
+                                          "traffic": load_traffic("k1_smooth_quant.hip", args.workload)},
+            "k2_w4a4_gemm": {"avg_launch_us": round(k2_ms * 1e3, 3), "int8_ops": ops_main,
+                             "achieved_TOPS": round(k2_achieved, 2)},
+        },
+        "wall_s_timed": round(wall, 4),
+        "pack_s": round(pack_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, X, pk, b, seconds):
+    """The CPU oracle (as it stands) on a bounded sample of rows of the same workload."""
+    from oracle import svdq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    rows = 16
+    t0 = time.perf_counter()
+    O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.M, max(16, rows * seconds / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * w.N * w.K + 2.0 * rows * w.rank * (w.K + w.N)
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(rows / dt, 2),
+            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{rows} of {w.M} token rows of {w.name} (full K={w.K}, N={w.N}, r={w.rank}), float64 numpy oracle"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+"""Python binding of libsvdq.so, the SVDQuant W4A4 linear layer for MI355X (gfx950).
+
+Argument marshalling only: every computation runs in the library (host
+packer in C++, forward in HIP kernels).  The functions carry the C ABI's
+names and argument order (see include/svdq.h).  Host functions take numpy
+arrays; device functions take torch tensors that already live on the GPU
+(torch only supplies device memory and the current stream).
+
+The library must be built first (``python -m bit_diffusion_model_svdq_amd.build``);
+importing this package without it raises an ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with python -m bit_diffusion_model_svdq_amd.build")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SVDQ_OK = 0
+STATUS_NAMES = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
+                3: "SVDQ_ERR_ALIGNMENT", 4: "SVDQ_ERR_WORKSPACE", 5: "SVDQ_ERR_NO_CONVERGENCE",
+                6: "SVDQ_ERR_HIP"}
+
+EXPORTS = [
+    "svdq_act_absmax_update", "svdq_pack_weights", "svdq_quantize_residual",
+    "svdq_forward_workspace_bytes", "svdq_linear_forward", "svdq_forward_quantize",
+    "svdq_forward_gemm", "svdq_quantize_activations", "svdq_debug_group_partials",
+    "svdq_status_string", "svdq_last_error",
+]
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.svdq_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+class svdq_pack_params(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("rank", ctypes.c_int), ("group", ctypes.c_int),
+                ("s_min", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_sig = {
+    "svdq_act_absmax_update": [_P, ctypes.c_int64, _I, _P],
+    "svdq_pack_weights": [_P, _I, _I, _P, ctypes.POINTER(svdq_pack_params), _P, _P, _P, _P, _P, _P],
+    "svdq_quantize_residual": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
+    "svdq_forward_workspace_bytes": [_I, _I, _I],
+    "svdq_linear_forward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_quantize": [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_quantize_activations": [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P],
+    "svdq_debug_group_partials": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "svdq_status_string": [_I],
+    "svdq_last_error": [],
+}
+for _name, _args in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _I
+_lib.svdq_forward_workspace_bytes.restype = ctypes.c_size_t
+_lib.svdq_status_string.restype = ctypes.c_char_p
+_lib.svdq_last_error.restype = ctypes.c_char_p
+
+
+def _check(st: int, where: str):
+    if st != SVDQ_OK:
+        raise SvdqError(st, where)
+
+
+# ------------------------------------------------------------------ host side
+def _host(a, dtype, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _hp(a):
+    return None if a is None else a.ctypes.data
+
+
+def svdq_act_absmax_update(X_bf16: np.ndarray, amax: np.ndarray) -> np.ndarray:
+    """Folds bf16 rows X [M, K] (uint16 bits) into the running abs-max amax [K] (float32, in place)."""
+    X = _host(X_bf16, np.uint16)
+    if amax.dtype != np.float32 or not amax.flags.c_contiguous or amax.shape != (X.shape[1],):
+        raise ValueError("amax must be a contiguous float32 [K] array")
+    _check(_lib.svdq_act_absmax_update(_hp(X), X.shape[0], X.shape[1], _hp(amax)), "svdq_act_absmax_update")
+    return amax
+
+
+def svdq_pack_weights(W: np.ndarray, act_absmax: np.ndarray, alpha: float = 0.5, rank: int = 32,
+                      s_min: float = 1e-5, group: int = 64, want_sigma: bool = False):
+    """Offline pack.  Returns dict(smooth, L1 [r,K] bf16 bits, L2 [N,r] bf16 bits, Wq, w_scales[, sigma])."""
+    W = _host(W, np.float32)
+    N, K = W.shape
+    A = _host(act_absmax, np.float32, (K,))
+    p = svdq_pack_params(alpha, rank, group, s_min)
+    out = dict(smooth=np.empty(K, np.float32), L1=np.empty((rank, K), np.uint16),
+               L2=np.empty((N, rank), np.uint16), Wq=np.empty((N, K // 2), np.uint8),
+               w_scales=np.empty((N, max(K // 64, 0)), np.float32))
+    sigma = np.empty(min(N, K), np.float64) if want_sigma else None
+    st = _lib.svdq_pack_weights(_hp(W), N, K, _hp(A), ctypes.byref(p), _hp(out["smooth"]),
+                                _hp(out["L1"]) if rank else None, _hp(out["L2"]) if rank else None,
+                                _hp(out["Wq"]), _hp(out["w_scales"]), _hp(sigma))
+    _check(st, "svdq_pack_weights")
+    if want_sigma:
+        out["sigma"] = sigma
+    return out
+
+
+def svdq_quantize_residual(W, smooth, L1, L2):
+    """Wq [N, K/2] and w_scales [N, K/64] from W, s, L1 [r, K], L2 [N, r] (host arrays)."""
+    W = _host(W, np.float32)
+    N, K = W.shape
+    s = _host(smooth, np.float32, (K,))
+    L1 = _host(L1, np.uint16)
+    L2 = _host(L2, np.uint16)
+    r = L1.shape[0] if L1.ndim == 2 else 0
+    Wq = np.empty((N, K // 2), np.uint8)
+    ws = np.empty((N, K // 64), np.float32)
+    st = _lib.svdq_quantize_residual(_hp(W), N, K, _hp(s), _hp(L1) if r else None,
+                                     _hp(L2) if r else None, r, _hp(Wq), _hp(ws))
+    _check(st, "svdq_quantize_residual")
+    return Wq, ws
+
+
+# ---------------------------------------------------------------- device side
+def _dp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def svdq_forward_workspace_bytes(M: int, K: int, r: int) -> int:
+    return int(_lib.svdq_forward_workspace_bytes(M, K, r))
+
+
+def svdq_linear_forward(X, smooth, L1, L2, Wq, w_scales, bias, Y, workspace, stream=None):
+    """Y [M, N] (bf16 tensor, written) = SVDQuant linear of X [M, K] bf16.  All tensors on the GPU."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_linear_forward(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                  _dp(w_scales), _dp(bias), _dp(Y), _dp(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_linear_forward")
+    return Y
+
+
+def svdq_forward_quantize(X, smooth, L1, workspace, stream=None):
+    M, K = X.shape
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_forward_quantize(_dp(X), M, K, r, _dp(smooth), _dp(L1), _dp(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_forward_quantize")
+
+
+def svdq_forward_gemm(M, K, L2, Wq, w_scales, bias, Y, workspace, r, stream=None):
+    N = Wq.shape[0]
+    st = _lib.svdq_forward_gemm(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_scales), _dp(bias), _dp(Y),
+                                _dp(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(st, "svdq_forward_gemm")
+
+
+def svdq_quantize_activations(X, smooth, L1, qx, sx, T, stream=None):
+    M, K = X.shape
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_quantize_activations(_dp(X), M, K, _dp(smooth), _dp(L1), r, _dp(qx), _dp(sx),
+                                        _dp(T), _stream(stream))
+    _check(st, "svdq_quantize_activations")
+
+
+def svdq_debug_group_partials(qx, Wq, m0, m1, n0, n1, P, stream=None):
+    M = qx.shape[0]
+    K = qx.shape[1] * 2
+    N = Wq.shape[0]
+    st = _lib.svdq_debug_group_partials(_dp(qx), _dp(Wq), M, N, K, m0, m1, n0, n1, _dp(P),
+                                        _stream(stream))
+    _check(st, "svdq_debug_group_partials")
+
+
+def svdq_status_string(status: int) -> str:
+    return _lib.svdq_status_string(status).decode()
+
+
+def svdq_last_error() -> str:
+    return _lib.svdq_last_error().decode()

@@ -1,0 +1,213 @@
+// C ABI entry points for the device side: argument validation, workspace
+// carving, kernel dispatch.  Host-side packing lives in pack.cpp.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "svdq_internal.h"
+
+namespace svdq {
+
+static thread_local char g_err[512] = "";
+
+svdq_status fail(svdq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+svdq_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SVDQ_OK;
+  return fail(SVDQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Workspace carve_workspace(void* base, int M, int K, int r) {
+  Workspace w;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  const size_t qx_bytes = align256((size_t)M * (K / 2));
+  const size_t sx_bytes = align256((size_t)M * (K / kGroup) * 4);
+  const size_t t_bytes = align256((size_t)M * r * 4);
+  w.qx = p;
+  w.sx = reinterpret_cast<float*>(p + qx_bytes);
+  w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
+  w.bytes = qx_bytes + sx_bytes + t_bytes;
+  return w;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+svdq_status check_shapes(int M, int K, int N, int r, bool need_n) {
+  if (M < 1) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 1 (got %d)", M);
+  if (K < kGroup || K % kGroup != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "K must be a positive multiple of 64 (got %d)", K);
+  if (need_n && (N < 16 || N % 16 != 0))
+    return fail(SVDQ_ERR_INVALID_ARG, "N must be a positive multiple of 16 (got %d)", N);
+  if (r < 0 || r > kMaxRank || r % 16 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "rank must be a multiple of 16 in [0, 128] (got %d)", r);
+  return SVDQ_OK;
+}
+
+svdq_status check_ptr(const void* p, const char* name, bool may_be_null) {
+  if (!p) {
+    if (may_be_null) return SVDQ_OK;
+    return fail(SVDQ_ERR_INVALID_ARG, "%s must not be NULL", name);
+  }
+  if (!aligned16(p)) return fail(SVDQ_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return SVDQ_OK;
+}
+
+#define SVDQ_TRY(expr)                   \
+  do {                                   \
+    const svdq_status st_ = (expr);      \
+    if (st_ != SVDQ_OK) return st_;      \
+  } while (0)
+
+svdq_status stage1_checks(const uint16_t* X, int M, int K, int r, const float* smooth,
+                          const uint16_t* L1) {
+  SVDQ_TRY(check_ptr(X, "X", false));
+  SVDQ_TRY(check_ptr(smooth, "smooth", false));
+  SVDQ_TRY(check_ptr(L1, "L1", r == 0));
+  (void)M;
+  (void)K;
+  return SVDQ_OK;
+}
+
+svdq_status stage2_checks(int r, const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
+                          const uint16_t* bias, const uint16_t* Y) {
+  SVDQ_TRY(check_ptr(L2, "L2", r == 0));
+  SVDQ_TRY(check_ptr(Wq, "Wq", false));
+  SVDQ_TRY(check_ptr(w_scales, "w_scales", false));
+  SVDQ_TRY(check_ptr(bias, "bias", true));
+  SVDQ_TRY(check_ptr(Y, "Y", false));
+  return SVDQ_OK;
+}
+
+template <class F>
+svdq_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (...) {
+    return fail(SVDQ_ERR_INVALID_ARG, "unexpected C++ exception");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svdq_forward_workspace_bytes(int M, int K, int r) {
+  if (M < 1 || K < kGroup || K % kGroup || r < 0 || r > kMaxRank || r % 16) return 0;
+  return carve_workspace(nullptr, M, K, r).bytes;
+}
+
+svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const float* smooth,
+                                  const uint16_t* L1, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, 16, r, false));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const Workspace w = carve_workspace(workspace, M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
+                                                   static_cast<hipStream_t>(stream)),
+                     "smooth_quant_lora_down launch");
+  });
+}
+
+svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                              const float* w_scales, const uint16_t* bias, uint16_t* Y,
+                              const void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, N, r, true));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y,
+                                      static_cast<hipStream_t>(stream)),
+                     "w4a4_gemm launch");
+  });
+}
+
+svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
+                                const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                const uint8_t* Wq, const float* w_scales, const uint16_t* bias,
+                                uint16_t* Y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return guarded([&]() -> svdq_status {
+    // validate everything before launching anything
+    SVDQ_TRY(check_shapes(M, K, N, r, true));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const Workspace w = carve_workspace(workspace, M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, s),
+                       "smooth_quant_lora_down launch"));
+    return hip_check(
+        launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y, s),
+        "w4a4_gemm launch");
+  });
+}
+
+svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const float* smooth,
+                                      const uint16_t* L1, int r, uint8_t* qx, float* sx,
+                                      float* T, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, 16, r, false));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(check_ptr(qx, "qx", false));
+    SVDQ_TRY(check_ptr(sx, "sx", false));
+    SVDQ_TRY(check_ptr(T, "T", r == 0));
+    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, qx, sx, T,
+                                                   static_cast<hipStream_t>(stream)),
+                     "smooth_quant_lora_down launch");
+  });
+}
+
+svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
+                                      int m0, int m1, int n0, int n1, int32_t* P, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, N, 0, true));
+    if (m0 < 0 || m1 > M || m0 >= m1 || n0 < 0 || n1 > N || n0 >= n1)
+      return fail(SVDQ_ERR_INVALID_ARG, "block [%d,%d)x[%d,%d) outside [0,%d)x[0,%d)", m0, m1, n0,
+                  n1, M, N);
+    SVDQ_TRY(check_ptr(qx, "qx", false));
+    SVDQ_TRY(check_ptr(Wq, "Wq", false));
+    SVDQ_TRY(check_ptr(P, "P", false));
+    return hip_check(
+        launch_group_partials(qx, Wq, M, N, K, m0, m1, n0, n1, P, static_cast<hipStream_t>(stream)),
+        "group_partials launch");
+  });
+}
+
+const char* svdq_status_string(svdq_status s) {
+  switch (s) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_INVALID_ARG: return "invalid argument";
+    case SVDQ_ERR_UNSUPPORTED: return "unsupported parameter";
+    case SVDQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_NO_CONVERGENCE: return "eigensolver did not converge";
+    case SVDQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* svdq_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "svdq.h"
+#include "svdq_errors.h"
+
+namespace svdq {
+
+constexpr int kGroup = 64;      // quantization group along K
+constexpr int kMaxRank = 128;   // rank bound of the low-rank branch
+
+svdq_status hip_check(hipError_t e, const char* what);
+
+// Workspace carving: qx [M, K/2] | sx [M, K/64] | T [M, r], each 256-byte aligned.
+struct Workspace {
+  uint8_t* qx;
+  float* sx;
+  float* T;
+  size_t bytes;
+};
+Workspace carve_workspace(void* base, int M, int K, int r);
+
+// k1: x_hat = X * (1/s); per-64 absmax, scales and codes; T = x_hat L1^T.
+hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
+                                         const float* smooth, const uint16_t* L1, uint8_t* qx,
+                                         float* sx, float* T, hipStream_t stream);
+
+// k2: Y = sum_g sx sw P_g + T L2^T + b, bf16 out.
+hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int M, int K,
+                            int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                            const float* w_scales, const uint16_t* bias, uint16_t* Y,
+                            hipStream_t stream);
+
+// k2's main loop with the integer group partials exported instead of the epilogue.
+hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
+                                 int m0, int m1, int n0, int n1, int32_t* P, hipStream_t stream);
+
+}  // namespace svdq

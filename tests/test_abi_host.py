@@ -1,0 +1,193 @@
+"""CPU tests of the C ABI: exported symbols, host-side packer parity with the oracle,
+and the argument validation of every entry point (no GPU needed: validation
+fails before anything is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import svdq_oracle as O
+
+S = pytest.importorskip("bit_diffusion_model_svdq_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, F64 = np.float32, np.float64
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(S.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(S.EXPORTS)
+
+
+def test_status_strings():
+    for st in range(7):
+        assert S.svdq_status_string(st) not in ("", "unknown status")
+    assert S.svdq_status_string(99) == "unknown status"
+
+
+# ------------------------------------------------------------------ packer
+def test_act_absmax_is_exact():
+    w = synth.WORKLOADS["tiny"]
+    Xc = synth.calibration_activations(w)
+    A = np.zeros(w.K, F32)
+    S.svdq_act_absmax_update(Xc[:100], A)
+    S.svdq_act_absmax_update(Xc[100:], A)     # streaming in two batches
+    np.testing.assert_array_equal(A, O.act_absmax(Xc))
+
+
+@pytest.mark.parametrize("N,K,r", [(1024, 1024, 16), (192, 320, 32), (320, 192, 16), (128, 256, 0)])
+def test_quantize_residual_bit_exact(N, K, r):
+    w = synth.WORKLOADS["tiny"]
+    W = synth.weight(w)[:N, :K]
+    A = O.act_absmax(synth.calibration_activations(w))[:K]
+    po = O.pack_weights(W, A, 0.5, rank=r)
+    Wq, ws = S.svdq_quantize_residual(W, po["s"], po["L1"], po["L2"])
+    np.testing.assert_array_equal(Wq, po["Wq"])
+    np.testing.assert_array_equal(ws.view(np.uint32), po["w_scales"].view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,r", [(1024, 1024, 16), (192, 320, 32), (320, 192, 16)])
+def test_pack_weights_matches_oracle(N, K, r):
+    w = synth.WORKLOADS["tiny"]
+    W = synth.weight(w)[:N, :K]
+    A = O.act_absmax(synth.calibration_activations(w))[:K]
+    pl = S.svdq_pack_weights(W, A, 0.5, r, want_sigma=True)
+    po = O.pack_weights(W, A, 0.5, rank=r)
+    np.testing.assert_array_equal(pl["smooth"], po["s"])
+    p = min(N, K)
+    # leading singular values to 1e-12 (the Gram route is accurate for sigma near sigma_1)
+    np.testing.assert_allclose(pl["sigma"][:2 * r], po["sigma"][:2 * r], rtol=1e-12)
+    np.testing.assert_allclose(pl["sigma"][:p], po["sigma"][:p], atol=1e-6 * po["sigma"][0])
+    # factors are not unique; their product is (bf16 rounding aside)
+    Ll = O.bf16_to_f64(pl["L2"]) @ O.bf16_to_f64(pl["L1"])
+    Lo = O.bf16_to_f64(po["L2"]) @ O.bf16_to_f64(po["L1"])
+    assert np.linalg.norm(Ll - Lo) <= 1e-3 * np.linalg.norm(Lo)
+    # Eckart-Young (E6) with the library's own factors, up to bf16 rounding of the factors
+    What = po["What"]
+    tail = float(np.sum(po["sigma"][r:] ** 2))
+    err2 = float(np.sum((What - Ll) ** 2))
+    assert abs(err2 - tail) <= 2 ** -6 * np.sqrt(tail * float(np.sum(po["sigma"][:r] ** 2))) + 1e-9
+    # lora_down rows orthonormal to bf16 accuracy
+    L1 = O.bf16_to_f64(pl["L1"])
+    np.testing.assert_allclose(L1 @ L1.T, np.eye(r), atol=2e-2)
+    # with identical factors the quantized residual is bit-identical
+    if np.array_equal(pl["L1"], po["L1"]) and np.array_equal(pl["L2"], po["L2"]):
+        np.testing.assert_array_equal(pl["Wq"], po["Wq"])
+        np.testing.assert_array_equal(pl["w_scales"], po["w_scales"])
+
+
+def test_pack_exact_lowrank_weight_leaves_zero_residual():
+    """W = L2 L1 with dyadic factors and s = 1: the library's own SVD must absorb all of it."""
+    K, N, r = 256, 192, 16
+    W = np.zeros((N, K), F32)
+    g = synth.rng_for("tiny", 20)
+    rows = g.choice(N, r, replace=False)
+    cols = g.choice(K, r, replace=False)
+    vals = 2.0 ** -np.arange(1, r + 1)
+    W[rows, cols] = vals                           # a scaled partial permutation: sigma = vals
+    A = O.weight_absmax(W)                         # A == W_scale -> s = 1 for alpha = 1/2
+    pl = S.svdq_pack_weights(W, A, 0.5, r, want_sigma=True)
+    np.testing.assert_array_equal(pl["smooth"], np.ones(K, F32))
+    np.testing.assert_allclose(pl["sigma"][:r], vals, rtol=1e-12)
+    assert np.all(pl["sigma"][r:] < 1e-6)
+    # what is left is round-off of the floating-point eigenvectors, ~1e-40 against entries of 2^-16..2^-1
+    assert float(np.max(pl["w_scales"])) < 1e-30
+
+
+@pytest.mark.slow
+def test_pack_weights_dit_projection_shape():
+    w = synth.WORKLOADS["dit_proj"]
+    W = synth.weight(w)
+    A = np.zeros(w.K, F32)
+    S.svdq_act_absmax_update(synth.calibration_activations(w), A)
+    pl = S.svdq_pack_weights(W, A, w.alpha, w.rank, want_sigma=True)
+    po = O.pack_weights(W, O.act_absmax(synth.calibration_activations(w)), w.alpha, rank=w.rank)
+    np.testing.assert_array_equal(pl["smooth"], po["s"])
+    np.testing.assert_allclose(pl["sigma"][:64], po["sigma"][:64], rtol=1e-12)
+    Ll = O.bf16_to_f64(pl["L2"]) @ O.bf16_to_f64(pl["L1"])
+    Lo = O.bf16_to_f64(po["L2"]) @ O.bf16_to_f64(po["L1"])
+    assert np.linalg.norm(Ll - Lo) <= 1e-3 * np.linalg.norm(Lo)
+    Wq, ws = S.svdq_quantize_residual(W, po["s"], po["L1"], po["L2"])
+    np.testing.assert_array_equal(Wq, po["Wq"])
+    np.testing.assert_array_equal(ws.view(np.uint32), po["w_scales"].view(np.uint32))
+
+
+# -------------------------------------------------------- validation errors
+def _status(fn, *args):
+    return getattr(S._lib, fn)(*args)
+
+
+def test_pack_rejects_bad_arguments_and_writes_nothing():
+    W = np.ones((64, 128), F32)
+    A = np.ones(128, F32)
+    outs = dict(s=np.full(128, 7, F32), L1=np.full((16, 128), 7, np.uint16), L2=np.full((64, 16), 7, np.uint16),
+                Wq=np.full((64, 64), 7, np.uint8), ws=np.full((64, 2), 7, F32))
+
+    def call(N=64, K=128, rank=16, group=64, alpha=0.5, smin=1e-5, Wp=True):
+        p = S.svdq_pack_params(alpha, rank, group, smin)
+        return S._lib.svdq_pack_weights(W.ctypes.data if Wp else None, N, K, A.ctypes.data, ctypes.byref(p),
+                                        outs["s"].ctypes.data, outs["L1"].ctypes.data, outs["L2"].ctypes.data,
+                                        outs["Wq"].ctypes.data, outs["ws"].ctypes.data, None)
+
+    assert call(group=32) == 2                    # SVDQ_ERR_UNSUPPORTED
+    assert call(K=100) == 1
+    assert call(rank=17) == 1
+    assert call(rank=144) == 1
+    assert call(alpha=1.5) == 1
+    assert call(smin=0.0) == 1
+    assert call(Wp=False) == 1
+    assert "NULL" in S.svdq_last_error()
+    for a in outs.values():
+        assert np.all(a == 7)
+    with pytest.raises(S.SvdqError):
+        S.svdq_quantize_residual(np.ones((8, 96), F32), np.ones(96, F32), np.zeros((0, 96), np.uint16),
+                                 np.zeros((8, 0), np.uint16))
+
+
+def test_workspace_bytes():
+    M, K, r = 4096, 3072, 32
+    b = S.svdq_forward_workspace_bytes(M, K, r)
+    al = lambda x: (x + 255) // 256 * 256
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(M * r * 4)
+    assert S.svdq_forward_workspace_bytes(M, 100, r) == 0
+    assert S.svdq_forward_workspace_bytes(M, K, 24) == 0
+
+
+def test_device_entry_points_validate_before_launching():
+    """Each case fails validation, so nothing reaches the GPU runtime."""
+    L = S._lib
+    a = 1 << 20            # a fake 16-byte-aligned address; never dereferenced
+    mis = a + 4
+    ws = S.svdq_forward_workspace_bytes(256, 1024, 16)
+    fwd = lambda X=a, M=256, K=1024, N=1024, r=16, L1=a, L2=a, bias=a, wsb=ws: L.svdq_linear_forward(
+        X, M, K, N, r, a, L1, L2, a, a, bias, a, a, wsb, None)
+    assert fwd(K=1000) == 1
+    assert fwd(M=0) == 1
+    assert fwd(N=1000) == 1
+    assert fwd(r=24) == 1
+    assert fwd(r=144) == 1
+    assert fwd(L1=None) == 1
+    assert fwd(X=mis) == 3
+    assert fwd(bias=mis) == 3
+    assert fwd(wsb=ws - 1) == 4
+    assert "workspace" in S.svdq_last_error()
+    assert L.svdq_forward_quantize(a, 256, 1000, 16, a, a, a, ws, None) == 1
+    assert L.svdq_forward_gemm(256, 1024, 1000, 16, a, a, a, None, a, a, ws, None) == 1
+    assert L.svdq_quantize_activations(a, 256, 1024, a, None, 16, a, a, a, None) == 1
+    assert L.svdq_quantize_activations(a, 256, 1024, a, a, 16, a, a, None, None) == 1
+    assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 0, 300, 0, 16, a, None) == 1
+    assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 10, 10, 0, 16, a, None) == 1
+    assert L.svdq_debug_group_partials(a, mis, 256, 1024, 1024, 0, 16, 0, 16, a, None) == 3

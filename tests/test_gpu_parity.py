@@ -1,0 +1,253 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: activation codes and scales (k1), integer group partial sums
+(k2's MFMA main loop).  Within tolerance: T = x_hat L1^T and the bf16 output
+Y (relative Frobenius error <= 5e-3 and max |error| <= 1e-2 max |Y_ref|).
+Packed weights come from the oracle's pack, so every input and every
+expected value is the oracle's.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import svdq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+S = pytest.importorskip("bit_diffusion_model_svdq_amd")
+
+F32, F64 = np.float32, np.float64
+Y_REL_FRO = 5e-3
+Y_MAX_ABS = 1e-2
+T_REL_FRO = 1e-4
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t, dtype):
+    return t.cpu().numpy().view(dtype)
+
+
+_PACK_CACHE = {}
+
+
+def packed(name, rank=None, M=None, K=None, N=None):
+    """Oracle-packed layer for a workload (optionally a sub-block of it)."""
+    key = (name, rank, M, K, N)
+    if key in _PACK_CACHE:
+        return _PACK_CACHE[key]
+    w = synth.WORKLOADS[name]
+    r = w.rank if rank is None else rank
+    X = synth.activations(w)
+    W = synth.weight(w)
+    b = synth.bias(w)
+    Xc = synth.calibration_activations(w)
+    M = M or w.M
+    K = K or w.K
+    N = N or w.N
+    X, W, b, Xc = X[:M, :K], W[:N, :K], b[:N], Xc[:, :K]
+    pk = O.pack_weights(W, O.act_absmax(Xc), w.alpha, rank=r)
+    res = dict(X=X, W=W, b=b, r=r, M=M, K=K, N=N, **{k: pk[k] for k in ("s", "L1", "L2", "Wq", "w_scales")})
+    _PACK_CACHE[key] = res
+    return res
+
+
+def to_device(p):
+    d = dict(X=dev(p["X"]), s=dev(p["s"]), Wq=dev(p["Wq"]), ws=dev(p["w_scales"]), b=dev(p["b"]))
+    d["L1"] = dev(p["L1"]) if p["r"] > 0 else None
+    d["L2"] = dev(p["L2"]) if p["r"] > 0 else None
+    return d
+
+
+def run_k1(p, d):
+    M, K, r = p["M"], p["K"], p["r"]
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    sx = torch.empty((M, K // 64), dtype=torch.float32, device=DEV)
+    T = torch.empty((M, max(r, 1)), dtype=torch.float32, device=DEV)
+    S.svdq_quantize_activations(d["X"], d["s"], d["L1"], qx, sx, T if r else None)
+    torch.cuda.synchronize()
+    return qx.cpu().numpy(), sx.cpu().numpy(), T.cpu().numpy()[:, :r]
+
+
+def run_forward(p, d, with_bias=True):
+    M, K, N, r = p["M"], p["K"], p["N"], p["r"]
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"] if with_bias else None,
+                          Y, ws)
+    torch.cuda.synchronize()
+    return O.bf16_to_f64(host(Y, np.uint16))
+
+
+def check_y(Yg, Yref, label):
+    rf, ma = O.rel_fro(Yg, Yref), O.max_abs_ratio(Yg, Yref)
+    say(f"{label}: rel_fro {rf:.3e} max_abs/max {ma:.3e}")
+    assert rf <= Y_REL_FRO and ma <= Y_MAX_ABS
+
+
+# ------------------------------------------------------------------- k1
+@pytest.mark.parametrize("name", ["tiny", "smallk_640", "smallk_1280", "dit_proj"])
+def test_k1_codes_scales_bit_exact_and_T(name):
+    say(f"k1 {name}")
+    p = packed(name)
+    d = to_device(p)
+    qx, sx, T = run_k1(p, d)
+    qx_o, sx_o, T_o, _ = O.quantize_activations(p["X"], p["s"], p["L1"])
+    np.testing.assert_array_equal(qx, qx_o)
+    np.testing.assert_array_equal(sx.view(np.uint32), sx_o.view(np.uint32))
+    assert O.rel_fro(T, T_o) <= T_REL_FRO
+
+
+def test_k1_power_of_two_equivariance_on_gpu():
+    p = dict(packed("tiny"))
+    d = to_device(p)
+    qx0, sx0, _ = run_k1(p, d)
+    p4 = dict(p, X=synth.f32_to_bf16_bits(O.bf16_to_f32(p["X"]) * F32(4)))
+    d4 = to_device(p4)
+    qx1, sx1, _ = run_k1(p4, d4)
+    np.testing.assert_array_equal(qx1, qx0)
+    np.testing.assert_array_equal(sx1, sx0 * F32(4))
+
+
+# --------------------------------------------------------- group partials
+def run_partials(qx_np, wq_np, m0, m1, n0, n1):
+    qx, wq = dev(qx_np), dev(wq_np)
+    G = qx_np.shape[1] * 2 // 64
+    P = torch.empty(((m1 - m0), (n1 - n0), G), dtype=torch.int32, device=DEV)
+    S.svdq_debug_group_partials(qx, wq, m0, m1, n0, n1, P)
+    torch.cuda.synchronize()
+    return P.cpu().numpy()
+
+
+def test_group_partials_bit_exact_tiny_full():
+    say("partials tiny")
+    p = packed("tiny")
+    qx_o, _, _, _ = O.quantize_activations(p["X"], p["s"])
+    P = run_partials(qx_o, p["Wq"], 0, p["M"], 0, p["N"])
+    np.testing.assert_array_equal(P, O.group_partials(qx_o, p["Wq"]))
+
+
+def test_group_partials_extremes():
+    """All codes -7 against +7: |P| reaches 64 * 49 in every group."""
+    qx = O.pack_nibbles(np.full((32, 256), -7, np.int8))
+    codes = np.tile(np.array([7, -7], np.int8), (48, 128))
+    codes[:16] = 7
+    codes[16:32] = -7
+    wq = O.pack_nibbles(codes)
+    P = run_partials(qx, wq, 0, 32, 0, 48)
+    np.testing.assert_array_equal(P, O.group_partials(qx, wq))
+    assert P.min() == -3136 and P.max() == 3136
+
+
+@pytest.mark.parametrize("blk", [(0, 128, 0, 128), (1000, 1100, 3000, 3072), (3968, 4096, 1536, 1664),
+                                 (17, 18, 5, 21)])
+def test_group_partials_dit_proj_blocks(blk):
+    say(f"partials dit_proj {blk}")
+    p = packed("dit_proj")
+    m0, m1, n0, n1 = blk
+    qx_o, _, _, _ = O.quantize_activations(p["X"][m0:m1], p["s"])
+    qx_full = np.zeros((p["M"], p["K"] // 2), np.uint8)
+    qx_full[m0:m1] = qx_o
+    P = run_partials(qx_full, p["Wq"], m0, m1, n0, n1)
+    np.testing.assert_array_equal(P, O.group_partials(qx_o, p["Wq"][n0:n1]))
+
+
+# ----------------------------------------------------------------- forward
+def test_forward_tiny_full():
+    say("forward tiny")
+    p = packed("tiny")
+    d = to_device(p)
+    Yg = run_forward(p, d)
+    Yref = O.forward(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg, Yref, "tiny")
+
+
+@pytest.mark.parametrize("name", ["smallk_640", "smallk_1280"])
+def test_forward_small_k_full(name):
+    say(f"forward {name}")
+    p = packed(name)
+    d = to_device(p)
+    Yg = run_forward(p, d)
+    Yref = O.forward(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg, Yref, name)
+
+
+def test_forward_dit_proj_sampled_rows():
+    """Full 4096x3072x3072 launch (the benchmarked configuration); rows checked on a sample."""
+    say("forward dit_proj")
+    p = packed("dit_proj")
+    d = to_device(p)
+    Yg = run_forward(p, d)
+    g = synth.rng_for("dit_proj", 30)
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(p["M"] - 16, p["M"]),
+                                     g.choice(p["M"], 480, replace=False)]))
+    Yref = O.forward(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg[rows], Yref, "dit_proj sampled")
+    Yx = O.forward_exact(p["X"][rows], p["W"], p["b"])
+    say(f"dit_proj method error vs X W^T + b: gpu {O.rel_fro(Yg[rows], Yx):.4f} oracle {O.rel_fro(Yref, Yx):.4f}")
+
+
+@pytest.mark.parametrize("M,K,N,r", [(200, 640, 208, 48), (1, 64, 16, 16), (77, 192, 48, 0), (300, 256, 144, 128)])
+def test_forward_ragged_shapes(M, K, N, r):
+    """Partial row tiles, partial K stages (K/64 not a multiple of 4), N not a multiple of 128,
+    r = 48 (odd number of 16-wide k-steps), r = 0 (no branch), r = 128 (the bound), M = 1."""
+    say(f"forward ragged {M}x{K}x{N} r={r}")
+    w = synth.WORKLOADS["tiny"]
+    X = synth.activations(w)[:M, :K]
+    W = synth.weight(w)[:N, :K]
+    b = synth.bias(w)[:N]
+    A = O.act_absmax(synth.calibration_activations(w)[:, :K])
+    pk = O.pack_weights(W, A, 0.5, rank=r)
+    p = dict(X=X, b=b, r=r, M=M, K=K, N=N, s=pk["s"], L1=pk["L1"], L2=pk["L2"], Wq=pk["Wq"],
+             w_scales=pk["w_scales"])
+    d = to_device(p)
+    qx, sx, T = run_k1(p, d)
+    qx_o, sx_o, T_o, _ = O.quantize_activations(X, pk["s"], pk["L1"])
+    np.testing.assert_array_equal(qx, qx_o)
+    np.testing.assert_array_equal(sx, sx_o)
+    Yg = run_forward(p, d)
+    Yref = O.forward(X, pk["s"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+    check_y(Yg, Yref, f"ragged {M}x{K}x{N} r={r}")
+    P = run_partials(qx_o, pk["Wq"], 0, M, 0, N)
+    np.testing.assert_array_equal(P, O.group_partials(qx_o, pk["Wq"]))
+
+
+def test_forward_without_bias_and_deterministic():
+    p = packed("tiny")
+    d = to_device(p)
+    Y1 = run_forward(p, d, with_bias=False)
+    Y2 = run_forward(p, d, with_bias=False)
+    np.testing.assert_array_equal(Y1, Y2)
+    Yref = O.forward(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], None)
+    check_y(Y1, Yref, "tiny no bias")
+
+
+def test_forward_stages_match_fused_call():
+    p = packed("smallk_640")
+    d = to_device(p)
+    Yf = run_forward(p, d)
+    M, K, N, r = p["M"], p["K"], p["N"], p["r"]
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    S.svdq_forward_quantize(d["X"], d["s"], d["L1"], ws)
+    S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], Y, ws, r)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(O.bf16_to_f64(host(Y, np.uint16)), Yf)
