@@ -9,13 +9,20 @@
 // Here X is read from HBM exactly once.
 //
 // Work split: one workgroup owns 16 rows (one MFMA row tile) and all of K;
-// its 8 waves take every 8th 64-channel group.  In a wave, lane l holds row
-// (l % 16) and the 16 consecutive channels 16 * (l / 16) .. +15 of the group,
-// so the group's absmax is a 16-element local max plus two cross-lane steps,
-// and the same registers are already the A operand of the bf16 MFMA (any
-// channel order that A and B share leaves the dot product unchanged).
-// x_hat enters the MFMA as a bf16 hi/lo pair, so T keeps ~16 significant bits.
-// The 8 waves' T partials are summed in LDS in a fixed order (deterministic).
+// each of its 8 waves takes a contiguous run of 64-channel groups and keeps
+// the next group's loads in flight while it works on the current one.  Lane
+// l holds row (l % 16) and, of each group, channels 8 * (l / 16) + 0..7 and
+// 32 + 8 * (l / 16) + 0..7: exactly the A operand layout of two 16x16x32 bf16
+// MFMAs, and two 16-byte loads that cover 64 contiguous bytes per row.  The
+// group absmax is a local max plus two cross-lane steps.
+//
+// Rounding to the integer code uses the float32 adder: for |y| <= 7.0000005,
+// fl32(y + 1.5 * 2^23) = 1.5 * 2^23 + rne(y) exactly, so the low byte of its
+// bit pattern is the code as an int8 and its low nibble is the packed code.
+// |y| cannot exceed 7 * (1 + 2^-24) because inv = fl32(7 / amax), so no clamp
+// is needed.  x_hat enters the MFMA as a bf16 hi/lo pair, so T keeps ~16
+// significant bits.  The 8 waves' T partials are summed in LDS in a fixed
+// order (deterministic).
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -27,9 +34,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kRows = 16;
 constexpr int kThreads = kWaves * 64;
-
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -37,12 +42,24 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
+// Two codes per byte from the rounding adder's results (low nibble = even channel).
+__device__ inline uint32_t nib2(float ze, float zo) {
+  const uint32_t e = __float_as_uint(ze), o = __float_as_uint(zo);
+  return (e & 0x0Fu) | ((o << 4) & 0xF0u);
+}
+
+__device__ inline uint32_t pack8(const float* z) {  // 8 codes -> one dword
+  const uint32_t b0 = nib2(z[0], z[1]), b1 = nib2(z[2], z[3]);
+  const uint32_t b2 = nib2(z[4], z[5]), b3 = nib2(z[6], z[7]);
+  return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+}
+
 template <int RT>  // RT = r / 16 column tiles of T
 __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, float* __restrict__ sx,
     float* __restrict__ T) {
-  extern __shared__ float lds[];  // inv_s [K] | T partials [kWaves][16][r]
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // inv_s [K] | T partials [kWaves][16][r]
   float* inv_s = lds;
   float* tpart = lds + K;
 
@@ -51,42 +68,57 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   const int wave = tid >> 6;
   const int m0 = blockIdx.x * kRows;
   const int G = K / kGroup;
+  const int per_wave = (G + kWaves - 1) / kWaves;
+  const int g_begin = min(G, wave * per_wave);
+  const int g_end = min(G, g_begin + per_wave);
 
-  // fl32(1 / s[k]): IEEE division, computed once per workgroup.
+  // fl32(1 / s[k]): IEEE division, once per workgroup.
   for (int k = tid; k < K; k += kThreads) inv_s[k] = 1.0f / smooth[k];
-  __syncthreads();
 
   const int row = m0 + (lane & 15);
   const bool row_ok = row < M;
-  const int kseg = lane >> 4;
+  const int fk = lane >> 4;
+  const uint16_t* xrow = X + (size_t)row * K + 8 * fk;
   f32x4 acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = wave; g < G; g += kWaves) {
-    const int k0 = g * kGroup + kseg * 16;
-    uint4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(X + (size_t)row * K + k0);
-      xa = p[0];
-      xb = p[1];
+  // software pipeline: the loads of group g + 1 are in flight while g is processed
+  uint4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
+  if (row_ok && g_begin < g_end) {
+    xa = *reinterpret_cast<const uint4*>(xrow + g_begin * kGroup);
+    xb = *reinterpret_cast<const uint4*>(xrow + g_begin * kGroup + 32);
+  }
+  __syncthreads();  // inv_s ready
+
+  for (int g = g_begin; g < g_end; ++g) {
+    uint4 na = {0u, 0u, 0u, 0u}, nb = {0u, 0u, 0u, 0u};
+    if (row_ok && g + 1 < g_end) {
+      na = *reinterpret_cast<const uint4*>(xrow + (g + 1) * kGroup);
+      nb = *reinterpret_cast<const uint4*>(xrow + (g + 1) * kGroup + 32);
     }
-    const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    const float4* isp = reinterpret_cast<const float4*>(inv_s + k0);
-    float is[16];
+    uint4 lb[RT > 0 ? RT : 1][2];
+    if constexpr (RT > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 v = isp[i];
-      is[4 * i + 0] = v.x;
-      is[4 * i + 1] = v.y;
-      is[4 * i + 2] = v.z;
-      is[4 * i + 3] = v.w;
+      for (int t = 0; t < RT; ++t) {
+        const uint16_t* lp = L1 + (size_t)(t * 16 + (lane & 15)) * K + g * kGroup + 8 * fk;
+        lb[t][0] = *reinterpret_cast<const uint4*>(lp);
+        lb[t][1] = *reinterpret_cast<const uint4*>(lp + 32);
+      }
     }
+    const int k0 = g * kGroup + 8 * fk;
+    const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
     float xh[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xh[2 * i] = bf16_lo(w[i]) * is[2 * i];
-      xh[2 * i + 1] = bf16_hi(w[i]) * is[2 * i + 1];
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 i0 = *reinterpret_cast<const f32x4*>(inv_s + k0 + 32 * c);
+      const f32x4 i1 = *reinterpret_cast<const f32x4*>(inv_s + k0 + 32 * c + 4);
+      const float is[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xh[8 * c + 2 * i] = __uint_as_float(w[4 * c + i] << 16) * is[2 * i];
+        xh[8 * c + 2 * i + 1] = __uint_as_float(w[4 * c + i] & 0xFFFF0000u) * is[2 * i + 1];
+      }
     }
     float amax = 0.f;
 #pragma unroll
@@ -95,21 +127,19 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const float scale = amax / 7.0f;
     const float inv = amax > 0.f ? 7.0f / amax : 0.f;
-    uint32_t pk[2] = {0u, 0u};
+    float z[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float q = __builtin_rintf(xh[i] * inv);
-      q = fminf(fmaxf(q, -7.0f), 7.0f);
-      pk[i >> 3] |= (uint32_t(int(q)) & 0xFu) << (4 * (i & 7));
-    }
+    for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
     if (row_ok) {
-      *reinterpret_cast<uint2*>(qx + (size_t)row * (K / 2) + k0 / 2) = make_uint2(pk[0], pk[1]);
-      if (kseg == 0) sx[(size_t)row * G + g] = scale;
+      uint8_t* qrow = qx + (size_t)row * (K / 2) + g * 32 + 4 * fk;
+      *reinterpret_cast<uint32_t*>(qrow) = pack8(z);
+      *reinterpret_cast<uint32_t*>(qrow + 16) = pack8(z + 8);
+      if (fk == 0) sx[(size_t)row * G + g] = scale;
     }
     if constexpr (RT > 0) {
       bf16x8 ahi[2], alo[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float v = xh[8 * c + i];
@@ -117,19 +147,17 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
           ahi[c][i] = h;
           alo[c][i] = (__bf16)(v - (float)h);
         }
-      }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const int n = t * 16 + (lane & 15);
-        const uint4* lp = reinterpret_cast<const uint4*>(L1 + (size_t)n * K + k0);
-        const bf16x8 b0 = as_bf16x8(lp[0]);
-        const bf16x8 b1 = as_bf16x8(lp[1]);
+        const bf16x8 b0 = as_bf16x8(lb[t][0]), b1 = as_bf16x8(lb[t][1]);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[0], b0, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[0], b0, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[1], b1, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[1], b1, acc[t], 0, 0, 0);
       }
     }
+    xa = na;
+    xb = nb;
   }
 
   if constexpr (RT > 0) {
@@ -138,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     for (int t = 0; t < RT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        tpart[(wave * 16 + 4 * (lane >> 4) + i) * r + t * 16 + (lane & 15)] = acc[t][i];
+        tpart[(wave * 16 + 4 * fk + i) * r + t * 16 + (lane & 15)] = acc[t][i];
     __syncthreads();
     for (int e = tid; e < 16 * r; e += kThreads) {
       const int rr = e / r, c = e - (e / r) * r;
@@ -156,8 +184,8 @@ hipError_t launch_rt(const uint16_t* X, int M, int K, int r, const float* smooth
   const size_t lds = (size_t)K * 4 + (size_t)kWaves * 16 * r * 4;
   auto kern = smooth_quant_lora_down_kernel<RT>;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int blocks = (M + kRows - 1) / kRows;

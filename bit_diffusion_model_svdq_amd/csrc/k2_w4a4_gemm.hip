@@ -11,8 +11,9 @@
 // is one v_mfma_i32_16x16x64_i8.  The 4-bit codes are widened by a shift:
 // a nibble moved to the top of its byte is the int8 value 16 q, so the
 // product of two widened operands is 256 P exactly, and the two nibbles of a
-// byte land in different registers -- a channel permutation that A and B
-// share, which leaves each group's dot product unchanged.
+// byte land in different registers -- a channel permutation that both
+// operands share, which leaves each group's dot product unchanged.  The
+// widening happens once per workgroup, when a stage is copied into LDS.
 //
 // Scale epilogue.  Per output and group this is the expensive part: the
 // vector ALU is 1/16 of the int8 matrix rate per output-group.  The MFMA's
@@ -23,15 +24,17 @@
 // and  acc = fma(t, sx, acc).  Two VALU operations per output and group, no
 // integer-to-float conversion.  acc / 256 is taken once at the end.
 //
+// The finished tile is staged through LDS and leaves as 16-byte row segments.
+//
 // Low-rank branch.  acc is the accumulator input of bf16 MFMAs that add
 // T L2^T, with T split into a bf16 hi/lo pair (T keeps ~16 significant bits).
 //
-// Tiling: 128x128 outputs per workgroup, 4 waves of 64x64 (4x4 MFMA tiles),
-// 4 groups (128 bytes of codes per row) per pipeline stage, double-buffered
-// LDS with an XOR swizzle of 8-byte chunks so that the 16 rows a fragment
-// read touches fall in distinct banks.  Workgroups are remapped so that each
-// XCD (workgroups are dealt round-robin to the 8 XCDs) works on one compact
-// block of tiles, which keeps its share of qx and Wq in its own L2.
+// Tiling is a template: WM x WN waves, each owning TM x TN tiles of 16x16
+// (tokens x features); two groups per pipeline stage, double-buffered in LDS
+// with a 16-byte slot swizzle that keeps fragment reads conflict-free.
+// Workgroups are remapped so that each XCD (workgroups are dealt round-robin
+// to the 8 XCDs) works on one compact block of tiles, which keeps its share
+// of qx and Wq in its own L2.
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -41,32 +44,39 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int GPS = 4;             // groups per stage
-constexpr int ROWB = GPS * 32;     // code bytes per row per stage
-constexpr int kThreads = 256;
+constexpr int GS = 2;              // groups per pipeline stage
+constexpr int ROWB = 64;           // int8 bytes per row and group in LDS
 constexpr int kMagicBits = 0x4B400000;  // 1.5 * 2^23
 constexpr float kMagic = 12582912.0f;
 
-struct Smem {
-  uint8_t a[2][BM * ROWB];
-  uint8_t b[2][BN * ROWB];
-  float sx[2][GPS][BM];
-  float2 sw[2][GPS][BN];
+template <int WM_, int WN_, int TM_, int TN_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int BM = WM * TM * 16;   // tokens per workgroup
+  static constexpr int BN = WN * TN * 16;   // features per workgroup
+  static constexpr int THREADS = WM * WN * 64;
+  static constexpr int A_PANEL = BM * ROWB + 16;   // +16 B: the GS panels start in different banks
+  static constexpr int B_PANEL = BN * ROWB + 16;
+  static constexpr int A_BYTES = GS * A_PANEL;
+  static constexpr int B_BYTES = GS * B_PANEL;
+  static constexpr int STAGE = A_BYTES + B_BYTES + GS * BM * 4 + 2 * GS * BN * 4;
+  static constexpr int OUT = BM * BN * 2;           // bf16 output tile, staged at the end
+  static constexpr int LDS = (2 * STAGE > OUT ? 2 * STAGE : OUT);
+  static_assert(BM + BN <= THREADS, "one scale row or column per thread");
 };
 
-__device__ inline int swz(int row, int chunk) {  // byte offset of 8-byte chunk in a stage row
-  return row * ROWB + ((chunk ^ (row & 15)) << 3);
+using TileBig = Tile<4, 2, 4, 6>;    // 256 x 192, 8 waves
+using TileMed = Tile<2, 2, 4, 4>;    // 128 x 128, 4 waves
+using TileSmall = Tile<2, 2, 2, 2>;  //  64 x  64, 4 waves
+
+// byte offset of 16-byte slot `slot` (0..3) of row `row` within one group's panel
+__device__ inline int swz(int row, int slot) {
+  return row * ROWB + ((slot ^ ((row >> 1) & 3)) << 4);
 }
 
-__device__ inline i32x4 widen(uint2 v) {  // 16 nibbles -> 16 int8 of value 16 q
-  i32x4 r;
-  r[0] = (int)((v.x << 4) & 0xF0F0F0F0u);
-  r[1] = (int)((v.y << 4) & 0xF0F0F0F0u);
-  r[2] = (int)(v.x & 0xF0F0F0F0u);
-  r[3] = (int)(v.y & 0xF0F0F0F0u);
-  return r;
+__device__ inline uint4 widen_lo_hi(uint32_t a, uint32_t b) {  // 16 nibbles -> 16 int8 of value 16 q
+  return make_uint4((a << 4) & 0xF0F0F0F0u, (b << 4) & 0xF0F0F0F0u, a & 0xF0F0F0F0u,
+                    b & 0xF0F0F0F0u);
 }
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
@@ -75,11 +85,13 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
+__device__ inline i32x4 as_i32x4(uint4 v) {
+  i32x4 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
 }
 
-// Tile coordinates of this workgroup: XCD-compact, then grouped by 8 row tiles.
+// Tile coordinates of this workgroup: XCD-compact, then grouped by 8 token tiles.
 __device__ inline void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
   const int total = ntm * ntn;
   int id = blockIdx.x;
@@ -95,95 +107,191 @@ __device__ inline void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
 }
 
 // EXPORT = false: the forward.  EXPORT = true: write the group partials P of
-// rows [row0, row1) x columns [col0, col1) instead of the epilogue.
-template <bool EXPORT>
-__global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
+// tokens [row0, row1) x features [col0, col1) instead of the epilogue.
+template <class C, bool EXPORT>
+__global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ T,
     int K, int r, const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scales, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ Y, int ldy, int row0, int row1, int col0, int col1,
     int32_t* __restrict__ P) {
-  __shared__ Smem sm;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int G = K / kGroup;
   const int KB = K / 2;
-  const int ntm = (row1 - row0 + BM - 1) / BM;
-  const int ntn = (col1 - col0 + BN - 1) / BN;
-  int tm, tn;
-  tile_of_block(ntm, ntn, tm, tn);
-  const int m0 = row0 + tm * BM;
-  const int n0 = col0 + tn * BN;
-  const int stages = (G + GPS - 1) / GPS;
+  const int ntm = (row1 - row0 + C::BM - 1) / C::BM;
+  const int ntn = (col1 - col0 + C::BN - 1) / C::BN;
+  int tmi, tni;
+  tile_of_block(ntm, ntn, tmi, tni);
+  const int m0 = row0 + tmi * C::BM;
+  const int n0 = col0 + tni * C::BN;
+  const int stages = (G + GS - 1) / GS;
 
-  // ---- global -> register staging assignment
-  const int ld_row = tid >> 3;      // + 32 i
-  const int ld_q = tid & 7;         // 16-byte chunk within the stage row
-  uint4 ra[4], rb[4];
-  float rs[GPS];
+  auto stage_a = [&](int buf) { return lds + buf * C::STAGE; };
+  auto stage_b = [&](int buf) { return lds + buf * C::STAGE + C::A_BYTES; };
+  auto stage_sx = [&](int buf) {
+    return reinterpret_cast<float*>(lds + buf * C::STAGE + C::A_BYTES + C::B_BYTES);
+  };
+  auto stage_swn = [&](int buf) { return reinterpret_cast<float2*>(stage_sx(buf) + GS * C::BM); };
 
+  // ---- global -> register staging.  Thread t copies 16-byte piece (t % 4) of
+  // rows t/4, t/4 + RPP, ...: piece q holds half h = q % 2 of group q / 2.
+  constexpr int RPP = C::THREADS / 4;
+  constexpr int APASS = (C::BM + RPP - 1) / RPP;
+  constexpr int BPASS = (C::BN + RPP - 1) / RPP;
+  const int q = tid & 3;
+  const int lrow = tid >> 2;
+  const uint8_t* a_src = qx + (size_t)(m0 + lrow) * KB + q * 16;
+  const uint8_t* b_src = Wq + (size_t)(n0 + lrow) * KB + q * 16;
+  uint4 sa[APASS], sb[BPASS];
+  float ss[GS];
   auto gload = [&](int s) {
-    const int gv = min(GPS, G - s * GPS);
-    const bool q_ok = (ld_q >> 1) < gv;
+    const bool g_ok = s * GS + (q >> 1) < G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = ld_row + 32 * i;
-      const int m = m0 + rr, n = n0 + rr;
-      ra[i] = (q_ok && m < row1)
-                  ? *reinterpret_cast<const uint4*>(qx + (size_t)m * KB + s * ROWB + ld_q * 16)
-                  : make_uint4(0u, 0u, 0u, 0u);
-      rb[i] = (q_ok && n < col1)
-                  ? *reinterpret_cast<const uint4*>(Wq + (size_t)n * KB + s * ROWB + ld_q * 16)
-                  : make_uint4(0u, 0u, 0u, 0u);
+    for (int p = 0; p < APASS; ++p) {
+      const int row = lrow + p * RPP;
+      sa[p] = make_uint4(0u, 0u, 0u, 0u);
+      if ((p + 1) * RPP <= C::BM || row < C::BM)
+        if (g_ok && m0 + row < row1)
+          sa[p] = *reinterpret_cast<const uint4*>(a_src + (size_t)p * RPP * KB + s * (GS * 32));
+    }
+#pragma unroll
+    for (int p = 0; p < BPASS; ++p) {
+      const int row = lrow + p * RPP;
+      sb[p] = make_uint4(0u, 0u, 0u, 0u);
+      if ((p + 1) * RPP <= C::BN || row < C::BN)
+        if (g_ok && n0 + row < col1)
+          sb[p] = *reinterpret_cast<const uint4*>(b_src + (size_t)p * RPP * KB + s * (GS * 32));
     }
     if (!EXPORT) {
-      const int rr = tid & 127;
-      if (tid < 128) {
-        const int m = m0 + rr;
 #pragma unroll
-        for (int j = 0; j < GPS; ++j)
-          rs[j] = (j < gv && m < row1) ? sx[(size_t)m * G + s * GPS + j] : 0.f;
-      } else {
-        const int n = n0 + rr;
+      for (int j = 0; j < GS; ++j) ss[j] = 0.f;
+      if (tid < C::BM) {
+        const int m = m0 + tid;
+        if (m < row1)
 #pragma unroll
-        for (int j = 0; j < GPS; ++j)
-          rs[j] = (j < gv && n < col1) ? w_scales[(size_t)n * G + s * GPS + j] : 0.f;
+          for (int j = 0; j < GS; ++j)
+            if (s * GS + j < G) ss[j] = sx[(size_t)m * G + s * GS + j];
+      } else if (tid < C::BM + C::BN) {
+        const int n = n0 + tid - C::BM;
+        if (n < col1)
+#pragma unroll
+          for (int j = 0; j < GS; ++j)
+            if (s * GS + j < G) ss[j] = w_scales[(size_t)n * G + s * GS + j];
       }
     }
   };
   auto sstore = [&](int buf) {
+    const int g = q >> 1, h = q & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = ld_row + 32 * i;
-      *reinterpret_cast<uint2*>(&sm.a[buf][swz(rr, 2 * ld_q)]) = make_uint2(ra[i].x, ra[i].y);
-      *reinterpret_cast<uint2*>(&sm.a[buf][swz(rr, 2 * ld_q + 1)]) = make_uint2(ra[i].z, ra[i].w);
-      *reinterpret_cast<uint2*>(&sm.b[buf][swz(rr, 2 * ld_q)]) = make_uint2(rb[i].x, rb[i].y);
-      *reinterpret_cast<uint2*>(&sm.b[buf][swz(rr, 2 * ld_q + 1)]) = make_uint2(rb[i].z, rb[i].w);
+    for (int p = 0; p < APASS; ++p) {
+      const int row = lrow + p * RPP;
+      if ((p + 1) * RPP <= C::BM || row < C::BM) {
+        uint8_t* panel = stage_a(buf) + g * C::A_PANEL;
+        *reinterpret_cast<uint4*>(panel + swz(row, 2 * h)) = widen_lo_hi(sa[p].x, sa[p].y);
+        *reinterpret_cast<uint4*>(panel + swz(row, 2 * h + 1)) = widen_lo_hi(sa[p].z, sa[p].w);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < BPASS; ++p) {
+      const int row = lrow + p * RPP;
+      if ((p + 1) * RPP <= C::BN || row < C::BN) {
+        uint8_t* panel = stage_b(buf) + g * C::B_PANEL;
+        *reinterpret_cast<uint4*>(panel + swz(row, 2 * h)) = widen_lo_hi(sb[p].x, sb[p].y);
+        *reinterpret_cast<uint4*>(panel + swz(row, 2 * h + 1)) = widen_lo_hi(sb[p].z, sb[p].w);
+      }
     }
     if (!EXPORT) {
-      const int rr = tid & 127;
-      if (tid < 128) {
+      if (tid < C::BM) {
 #pragma unroll
-        for (int j = 0; j < GPS; ++j) sm.sx[buf][j][rr] = rs[j];
-      } else {
+        for (int j = 0; j < GS; ++j) stage_sx(buf)[j * C::BM + tid] = ss[j];
+      } else if (tid < C::BM + C::BN) {
+        const int col = tid - C::BM;
 #pragma unroll
-        for (int j = 0; j < GPS; ++j) sm.sw[buf][j][rr] = make_float2(rs[j], -kMagic * rs[j]);
+        for (int j = 0; j < GS; ++j) stage_swn(buf)[j * C::BN + col] = make_float2(ss[j], -kMagic * ss[j]);
       }
     }
   };
 
-  // ---- per-wave output tile
-  const int wr = (wave >> 1) * 64;
-  const int wc = (wave & 1) * 64;
-  const int fr = lane & 15;   // fragment row / column
-  const int fk = lane >> 4;   // fragment k slot
-  f32x4 acc[4][4];
+  // ---- per-wave output tile: TM token tiles x TN feature tiles
+  const int wm = wave / C::WN, wn = wave - (wave / C::WN) * C::WN;
+  const int wr = wm * C::TM * 16;   // token offset in the workgroup tile
+  const int wc = wn * C::TN * 16;   // feature offset
+  const int fr = lane & 15;
+  const int fk = lane >> 4;
+  f32x4 acc[C::TM][C::TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const i32x4 cmagic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
+
+  // One group: 16x16x64 int8 MFMAs over TM x TN tiles, software-pipelined so
+  // that the MFMAs of feature tile tn are in flight while the scale epilogue
+  // of tile tn - 1 runs on the VALU; the next tile's fragment is read from
+  // LDS one tile ahead.  MFMA result layout (16x16): lane l holds column
+  // l % 16 and rows 4 * (l / 16) + i, i = 0..3.
+  auto do_group = [&](int buf, int g, int gglob) {
+    const uint8_t* pa = stage_a(buf) + g * C::A_PANEL;
+    const uint8_t* pb = stage_b(buf) + g * C::B_PANEL;
+    const float2* pswn = stage_swn(buf) + g * C::BN + wc + fr;
+    i32x4 xf[C::TM];
+    f32x4 sxv[C::TM];
+#pragma unroll
+    for (int t = 0; t < C::TM; ++t) {
+      xf[t] = as_i32x4(*reinterpret_cast<const uint4*>(pa + swz(wr + 16 * t + fr, fk)));
+      if (!EXPORT)
+        sxv[t] = *reinterpret_cast<const f32x4*>(stage_sx(buf) + g * C::BM + wr + 16 * t + 4 * fk);
+    }
+    i32x4 wcur = as_i32x4(*reinterpret_cast<const uint4*>(pb + swz(wc + fr, fk)));
+    float2 swc = make_float2(0.f, 0.f);
+    if (!EXPORT) swc = pswn[0];
+    i32x4 dprev[C::TM];
+    float2 swp = swc;
+    auto epilogue = [&](const i32x4* d, float2 sw, int tn) {
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) {
+        if (EXPORT) {
+          const int n = n0 + wc + 16 * tn + fr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wr + 16 * tm + 4 * fk + i;
+            if (m < row1 && n < col1)
+              P[((size_t)(m - row0) * (col1 - col0) + (n - col0)) * G + gglob] =
+                  (d[tm][i] - kMagicBits) >> 8;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float t = __builtin_fmaf(__int_as_float(d[tm][i]), sw.x, sw.y);
+            acc[tm][tn][i] = __builtin_fmaf(t, sxv[tm][i], acc[tm][tn][i]);
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      i32x4 wnext = wcur;
+      float2 swn = swc;
+      if (tn + 1 < C::TN) {
+        wnext = as_i32x4(*reinterpret_cast<const uint4*>(pb + swz(wc + 16 * (tn + 1) + fr, fk)));
+        if (!EXPORT) swn = pswn[16 * (tn + 1)];
+      }
+      i32x4 dcur[C::TM];
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+        dcur[tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[tm], wcur, cmagic, 0, 0, 0);
+      if (tn > 0) epilogue(dprev, swp, tn - 1);
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) dprev[tm] = dcur[tm];
+      swp = swc;
+      wcur = wnext;
+      swc = swn;
+    }
+    epilogue(dprev, swp, C::TN - 1);
+  };
 
   gload(0);
   sstore(0);
@@ -192,72 +300,29 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
   for (int s = 0; s < stages; ++s) {
     const int buf = s & 1;
     if (s + 1 < stages) gload(s + 1);
-    const int gv = min(GPS, G - s * GPS);
-    for (int g = 0; g < gv; ++g) {
-      i32x4 af[4], bfr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ar = wr + 16 * t + fr;
-        af[t] = widen(*reinterpret_cast<const uint2*>(&sm.a[buf][swz(ar, 4 * g + fk)]));
-        const int br = wc + 16 * t + fr;
-        bfr[t] = widen(*reinterpret_cast<const uint2*>(&sm.b[buf][swz(br, 4 * g + fk)]));
-      }
-      if (EXPORT) {
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-          for (int tj = 0; tj < 4; ++tj) {
-            const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ti], bfr[tj], cmagic, 0, 0, 0);
-            const int n = n0 + wc + 16 * tj + fr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = m0 + wr + 16 * ti + 4 * fk + i;
-              if (m < row1 && n < col1)
-                P[((size_t)(m - row0) * (col1 - col0) + (n - col0)) * G + s * GPS + g] =
-                    (d[i] - kMagicBits) >> 8;
-            }
-          }
-      } else {
-        f32x4 sxv[4];
-        float2 swv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          sxv[t] = *reinterpret_cast<const f32x4*>(&sm.sx[buf][g][wr + 16 * t + 4 * fk]);
-          swv[t] = sm.sw[buf][g][wc + 16 * t + fr];
-        }
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-          for (int tj = 0; tj < 4; ++tj) {
-            const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ti], bfr[tj], cmagic, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float t = __builtin_fmaf(__int_as_float(d[i]), swv[tj].x, swv[tj].y);
-              acc[ti][tj][i] = __builtin_fmaf(t, sxv[ti][i], acc[ti][tj][i]);
-            }
-          }
-      }
-    }
+    const int gv = min(GS, G - s * GS);
+#pragma nounroll
+    for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
     if (s + 1 < stages) sstore(buf ^ 1);
     __syncthreads();
   }
 
   if (EXPORT) return;
 
-  // ---- epilogue: 1/256, + T L2^T (bf16 hi/lo MFMA), + bias, bf16 store
+  // ---- epilogue: 1/256, + L2 T^T (bf16 hi/lo MFMA), + bias, bf16 store
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+  for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj)
+    for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[ti][tj][i] *= (1.0f / 256.0f);
+      for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
 
   for (int j0 = 0; j0 < r; j0 += 32) {
     const int j = j0 + 8 * fk;
     const bool j_ok = j < r;
-    bf16x8 thi[4], tlo[4], lf[4];
+    bf16x8 thi[C::TM], tlo[C::TM];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < C::TM; ++t) {
       const int m = m0 + wr + 16 * t + fr;
       float tv[8];
       if (j_ok && m < row1) {
@@ -275,32 +340,107 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
         thi[t][e] = h;
         tlo[t][e] = (__bf16)(tv[e] - (float)h);
       }
-      const int n = n0 + wc + 16 * t + fr;
-      lf[t] = (j_ok && n < col1)
-                  ? as_bf16x8(*reinterpret_cast<const uint4*>(L2 + (size_t)n * r + j))
-                  : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int n = n0 + wc + 16 * tn + fr;
+      const bf16x8 lf = (j_ok && n < col1)
+                            ? as_bf16x8(*reinterpret_cast<const uint4*>(L2 + (size_t)n * r + j))
+                            : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[ti], lf[tj], acc[ti][tj], 0, 0, 0);
-        acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[ti], lf[tj], acc[ti][tj], 0, 0, 0);
+      for (int tm = 0; tm < C::TM; ++tm) {
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[tm], lf, acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[tm], lf, acc[tm][tn], 0, 0, 0);
       }
+    }
   }
 
+  // bias, bf16, then the tile goes through LDS (columns swizzled by 16 elements
+  // per group of 4 rows, so that the 4 row groups of a write hit distinct banks)
+  // and leaves as 16-byte row segments.
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-  for (int tj = 0; tj < 4; ++tj) {
-    const int n = n0 + wc + 16 * tj + fr;
-    if (n >= col1) continue;
-    const float bv = bias ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int col = wc + 16 * tn + fr;
+    const int n = n0 + col;
+    const float bv = (bias && n < col1) ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wr + 16 * ti + 4 * fk + i;
-        if (m < row1) Y[(size_t)m * ldy + n] = f32_to_bf16_rne(acc[ti][tj][i] + bv);
+        const int row = wr + 16 * tm + 4 * fk + i;
+        otile[row * C::BN + (col ^ (16 * ((row >> 2) & 3)))] =
+            __builtin_bit_cast(uint16_t, (__bf16)(acc[tm][tn][i] + bv));
       }
+  }
+  __syncthreads();
+  constexpr int CPR = C::BN / 8;   // 16-byte chunks per output row
+  for (int c = tid; c < C::BM * CPR; c += C::THREADS) {
+    const int row = c / CPR, ch = c - (c / CPR) * CPR;
+    const int m = m0 + row, n = n0 + 8 * ch;
+    if (m < row1 && n < col1) {
+      const uint4 v = *reinterpret_cast<const uint4*>(otile + row * C::BN + 8 * (ch ^ (2 * ((row >> 2) & 3))));
+      *reinterpret_cast<uint4*>(Y + (size_t)m * ldy + n) = v;
+    }
+  }
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <class C, bool EXPORT>
+hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int K, int r,
+                       const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
+                       const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
+                       int col1, int32_t* P, hipStream_t stream) {
+  auto kern = w4a4_gemm_kernel<C, EXPORT>;
+  static bool attr_set = false;  // benign race: every caller sets the same value
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((row1 - row0 + C::BM - 1) / C::BM) * ((col1 - col0 + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq,
+                     w_scales, bias, Y, ldy, row0, row1, col0, col1, P);
+  return hipGetLastError();
+}
+
+// Tile choice: the biggest tile that still gives every CU at least one workgroup.
+int pick_tile(int rows, int cols) {
+  const int cus = cu_count();
+  auto tiles = [&](int bm, int bn) { return ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn); };
+  if (tiles(TileBig::BM, TileBig::BN) >= cus) return 2;
+  if (tiles(TileMed::BM, TileMed::BN) >= cus) return 1;
+  return 0;
+}
+
+template <bool EXPORT>
+hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int K, int r,
+                    const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
+                    const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
+                    int col1, int32_t* P, hipStream_t stream) {
+  switch (pick_tile(row1 - row0, col1 - col0)) {
+    case 2:
+      return launch_tile<TileBig, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+                                          row1, col0, col1, P, stream);
+    case 1:
+      return launch_tile<TileMed, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+                                          row1, col0, col1, P, stream);
+    default:
+      return launch_tile<TileSmall, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+                                            row1, col0, col1, P, stream);
   }
 }
 
@@ -310,20 +450,16 @@ hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, 
                             int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
                             hipStream_t stream) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(w4a4_gemm_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream, qx, sx, T,
-                     K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N, nullptr);
-  return hipGetLastError();
+  return dispatch<false>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N, nullptr,
+                         stream);
 }
 
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                  int m0, int m1, int n0, int n1, int32_t* P, hipStream_t stream) {
   (void)M;
   (void)N;
-  const int tiles = ((m1 - m0 + BM - 1) / BM) * ((n1 - n0 + BN - 1) / BN);
-  hipLaunchKernelGGL(w4a4_gemm_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, qx, nullptr,
-                     nullptr, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0, m1, n0, n1, P);
-  return hipGetLastError();
+  return dispatch<true>(qx, nullptr, nullptr, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
+                        m1, n0, n1, P, stream);
 }
 
 }  // namespace svdq
