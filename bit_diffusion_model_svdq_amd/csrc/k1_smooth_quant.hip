@@ -9,8 +9,9 @@
 // Here X is read from HBM exactly once.
 //
 // Work split: one workgroup owns 16 rows (one MFMA row tile) and all of K;
-// each of its 8 waves takes a contiguous run of 64-channel groups and keeps
-// the next group's loads in flight while it works on the current one.  Lane
+// each of its 8 waves takes a contiguous run of 64-channel groups and issues
+// the loads of up to 6 groups at once (the whole run for K <= 3072), so
+// that a workgroup has its entire slice of X in flight.  Lane
 // l holds row (l % 16) and, of each group, channels 8 * (l / 16) + 0..7 and
 // 32 + 8 * (l / 16) + 0..7: exactly the A operand layout of two 16x16x32 bf16
 // MFMAs, and two 16-byte loads that cover 64 contiguous bytes per row.  The
@@ -20,8 +21,9 @@
 // fl32(y + 1.5 * 2^23) = 1.5 * 2^23 + rne(y) exactly, so the low byte of its
 // bit pattern is the code as an int8 and its low nibble is the packed code.
 // |y| cannot exceed 7 * (1 + 2^-24) because inv = fl32(7 / amax), so no clamp
-// is needed.  x_hat enters the MFMA as a bf16 hi/lo pair, so T keeps ~16
-// significant bits.  The 8 waves' T partials are summed in LDS in a fixed
+// is needed.  x_hat enters the MFMA as a bf16 hi/lo pair (hi = x_hat with the
+// low 16 bits cleared, lo = bf16(x_hat - hi), an exact difference), so T keeps
+// ~16 significant bits.  The 8 waves' T partials are summed in LDS in a fixed
 // order (deterministic).
 #include "svdq_internal.h"
 
@@ -35,6 +37,13 @@ constexpr int kWaves = 8;
 constexpr int kRows = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t cvt_bf16x2(float a, float b) {  // round-to-nearest-even pair
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -78,34 +87,20 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   const int row = m0 + (lane & 15);
   const bool row_ok = row < M;
   const int fk = lane >> 4;
-  const uint16_t* xrow = X + (size_t)row * K + 8 * fk;
+  // rows past M read row M-1 (never stored): every load is unconditional, so
+  // the compiler issues them back to back instead of draining at branch joins
+  const uint16_t* xrow = X + (size_t)min(row, M - 1) * K + 8 * fk;
   f32x4 acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // software pipeline: the loads of group g + 1 are in flight while g is processed
-  uint4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-  if (row_ok && g_begin < g_end) {
-    xa = *reinterpret_cast<const uint4*>(xrow + g_begin * kGroup);
-    xb = *reinterpret_cast<const uint4*>(xrow + g_begin * kGroup + 32);
-  }
   __syncthreads();  // inv_s ready
 
-  for (int g = g_begin; g < g_end; ++g) {
-    uint4 na = {0u, 0u, 0u, 0u}, nb = {0u, 0u, 0u, 0u};
-    if (row_ok && g + 1 < g_end) {
-      na = *reinterpret_cast<const uint4*>(xrow + (g + 1) * kGroup);
-      nb = *reinterpret_cast<const uint4*>(xrow + (g + 1) * kGroup + 32);
-    }
-    uint4 lb[RT > 0 ? RT : 1][2];
-    if constexpr (RT > 0) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const uint16_t* lp = L1 + (size_t)(t * 16 + (lane & 15)) * K + g * kGroup + 8 * fk;
-        lb[t][0] = *reinterpret_cast<const uint4*>(lp);
-        lb[t][1] = *reinterpret_cast<const uint4*>(lp + 32);
-      }
-    }
+  // Process one group whose X pieces (xa: channels 8fk..+7, xb: 32+8fk..+7) are in registers.
+  // The codes and the scale come back in registers: stores share the in-order
+  // vector-memory counter with loads, so a store issued here would make the
+  // next group's wait for its prefetched L1 fragments wait for the store too.
+  auto process = [&](int g, uint4 xa, uint4 xb, const uint4* lb, uint2& out, float& out_scale) {
     const int k0 = g * kGroup + 8 * fk;
     const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
     float xh[16];
@@ -130,34 +125,82 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     float z[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
-    if (row_ok) {
-      uint8_t* qrow = qx + (size_t)row * (K / 2) + g * 32 + 4 * fk;
-      *reinterpret_cast<uint32_t*>(qrow) = pack8(z);
-      *reinterpret_cast<uint32_t*>(qrow + 16) = pack8(z + 8);
-      if (fk == 0) sx[(size_t)row * G + g] = scale;
-    }
+    out.x = pack8(z);
+    out.y = pack8(z + 8);
+    out_scale = scale;
     if constexpr (RT > 0) {
-      bf16x8 ahi[2], alo[2];
+      uint32_t hi[8], lo[8];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float v = xh[8 * c + i];
-          const __bf16 h = (__bf16)v;
-          ahi[c][i] = h;
-          alo[c][i] = (__bf16)(v - (float)h);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b0 = __float_as_uint(xh[2 * i]), b1 = __float_as_uint(xh[2 * i + 1]);
+        hi[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // upper halves: truncated bf16 pair
+        lo[i] = cvt_bf16x2(xh[2 * i] - __uint_as_float(b0 & 0xFFFF0000u),
+                           xh[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u));
+      }
+      const bf16x8 ahi0 = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      const bf16x8 ahi1 = as_bf16x8(make_uint4(hi[4], hi[5], hi[6], hi[7]));
+      const bf16x8 alo0 = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+      const bf16x8 alo1 = as_bf16x8(make_uint4(lo[4], lo[5], lo[6], lo[7]));
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const bf16x8 b0 = as_bf16x8(lb[t][0]), b1 = as_bf16x8(lb[t][1]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[0], b0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[0], b0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[1], b1, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[1], b1, acc[t], 0, 0, 0);
+        const bf16x8 b0 = as_bf16x8(lb[2 * t]), b1 = as_bf16x8(lb[2 * t + 1]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi0, b0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo0, b0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi1, b1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo1, b1, acc[t], 0, 0, 0);
       }
     }
-    xa = na;
-    xb = nb;
+  };
+  constexpr int NL = RT > 0 ? 2 * RT : 1;
+  constexpr int kChunk = RT > 4 ? 3 : 6;  // groups whose X loads are in flight together
+  auto load_l1 = [&](int g, uint4* lb) {
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint16_t* lp = L1 + (size_t)(t * 16 + (lane & 15)) * K + g * kGroup + 8 * fk;
+        lb[2 * t] = *reinterpret_cast<const uint4*>(lp);
+        lb[2 * t + 1] = *reinterpret_cast<const uint4*>(lp + 32);
+      }
+    }
+  };
+
+  for (int c0 = g_begin; c0 < g_end; c0 += kChunk) {
+    // all X loads of the chunk first
+    uint4 xa[kChunk], xb[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int gj = min(c0 + j, g_end - 1);   // groups past the run re-read its last one (unused)
+      xa[j] = *reinterpret_cast<const uint4*>(xrow + gj * kGroup);
+      xb[j] = *reinterpret_cast<const uint4*>(xrow + gj * kGroup + 32);
+    }
+    uint4 lbc[NL], lbn[NL];
+#pragma unroll
+    for (int e = 0; e < NL; ++e) lbn[e] = make_uint4(0u, 0u, 0u, 0u);
+    load_l1(c0, lbc);
+    uint2 codes[kChunk];
+    float scales[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      codes[j] = make_uint2(0u, 0u);
+      scales[j] = 0.f;
+      if (c0 + j < g_end) {
+        if (j + 1 < kChunk && c0 + j + 1 < g_end) load_l1(c0 + j + 1, lbn);
+        process(c0 + j, xa[j], xb[j], lbc, codes[j], scales[j]);
+#pragma unroll
+        for (int e = 0; e < NL; ++e) lbc[e] = lbn[e];
+      }
+    }
+    if (row_ok) {
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (c0 + j < g_end) {
+          uint8_t* qrow = qx + (size_t)row * (K / 2) + (c0 + j) * 32 + 4 * fk;
+          *reinterpret_cast<uint32_t*>(qrow) = codes[j].x;
+          *reinterpret_cast<uint32_t*>(qrow + 16) = codes[j].y;
+          if (fk == 0) sx[(size_t)row * G + c0 + j] = scales[j];
+        }
+      }
+    }
   }
 
   if constexpr (RT > 0) {
