@@ -8,7 +8,9 @@ over more than 512 MB of buffers so that the 256 MB Infinity Cache cannot
 serve a step from the previous one.
 
 Prints one JSON line (rank 0).  Default workload: the DiT attention
-projection, M=4096 tokens, K=N=3072, rank 32.
+projection, M=4096 tokens, K=N=3072, rank 32.  Other workloads (--workload)
+are the small-K UNet widths and the DiT MLP linears; --graph replays whole
+rotations of steps from a HIP graph (for the launch-bound small shapes).
 """
 from __future__ import annotations
 
@@ -40,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from a HIP graph; value is then the graph rate")
     return ap.parse_args()
 
 
@@ -129,6 +133,7 @@ def main():
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
 
     # ---- timed region: K steps, HIP events on the launch stream around each kernel
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -152,17 +157,58 @@ def main():
     k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_step = total_ms / args.steps
+    eager_ms_step = ms_step
+
+    graph_info = None
+    if args.graph:
+        # one graph = one full rotation of steps; replayed back to back
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for d in sets:
+                step(d)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for d in sets:
+                step(d)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        replays = max(1, args.steps // nsets)
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(replays):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        ms_step = gs.elapsed_time(ge) / (replays * nsets)
+        graph_info = {"replays": replays, "steps_per_graph": nsets, "ms_per_step": round(ms_step, 5),
+                      "eager_ms_per_step": round(eager_ms_step, 5)}
 
     ops_main = 2.0 * M * N * K                 # int8 MFMA work of the W4A4 product
     ops_low = 2.0 * M * r * (K + N)            # bf16 low-rank branch
     tops = (ops_main + ops_low) / (ms_step * 1e-3) / 1e12
     tokens_s = M / (ms_step * 1e-3)
     k1_bytes = M * (2 * K + K // 2 + 4 * (K // 64) + 4 * r) + r * K * 2 + K * 4
-    k2_achieved = ops_main / (k2_ms * 1e-3) / 1e12
+    k2_bytes = (M * (K // 2 + 4 * (K // 64) + 4 * r + 2 * N)
+                + N * K // 2 + 4 * N * (K // 64) + 2 * r * (K + N) + 2 * N)
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
+    # k2's bound: whichever roofline floor is longer at this shape
+    k2_bound = "mfma" if ops_main / (PEAK_INT8_TOPS * 1e12) >= k2_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"
+    if k2_bound == "mfma":
+        k2_achieved, k2_peak, k2_unit = ops_main / (k2_ms * 1e-3) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
+    else:
+        k2_achieved, k2_peak, k2_unit = k2_bytes / (k2_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    k2_tops = ops_main / (k2_ms * 1e-3) / 1e12
+    if args.workload == "dit_proj":
+        metric = "fused W4A4+low-rank linear TOPS and tokens/s at M=4096,K=N=3072,r=32 (% MFMA peak)"
+    else:
+        metric = f"fused W4A4+low-rank linear TOPS and tokens/s at M={M},K={K},N={N},r={r} (% MFMA peak)"
 
     out = {
-        "metric": "fused W4A4+low-rank linear TOPS and tokens/s at M=4096,K=N=3072,r=32 (% MFMA peak)",
+        "metric": metric,
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -175,16 +221,17 @@ def main():
         "dtype": "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output",
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "group": 64,
-                   "rotated_sets": nsets},
+                   "rotated_sets": nsets, "hip_graph": bool(args.graph)},
         "tokens_per_s": round(tokens_s, 1),
         "pct_int8_mfma_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "roofline": {
             "kernel": "w4a4_gemm (k2)",
-            "bound": "mfma",
+            "bound": k2_bound,
             "achieved": round(k2_achieved, 2),
-            "peak": PEAK_INT8_TOPS,
-            "unit": "TFLOP/s",
-            "frac": round(k2_achieved / PEAK_INT8_TOPS, 4),
+            "peak": k2_peak,
+            "unit": k2_unit,
+            "frac": round(k2_achieved / k2_peak, 4),
+            "algorithmic": {"int8_ops": ops_main, "bytes": k2_bytes},
             "traffic": load_traffic("k2_w4a4_gemm.hip", args.workload),
             "avg_launch_us": round(k2_ms * 1e3, 3),
         },
@@ -194,8 +241,12 @@ def main():
                                           "peak_GBs": PEAK_HBM_GBS, "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
                                           "traffic": load_traffic("k1_smooth_quant.hip", args.workload)},
             "k2_w4a4_gemm": {"avg_launch_us": round(k2_ms * 1e3, 3), "int8_ops": ops_main,
-                             "achieved_TOPS": round(k2_achieved, 2)},
+                             "achieved_TOPS": round(k2_tops, 2),
+                             "pct_int8_peak": round(100.0 * k2_tops / PEAK_INT8_TOPS, 2),
+                             "algorithmic_bytes": k2_bytes,
+                             "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)},
         },
+        "graph": graph_info,
         "wall_s_timed": round(wall, 4),
         "pack_s": round(pack_s, 2),
     }
@@ -213,18 +264,26 @@ def cpu_baseline(w, X, pk, b, seconds):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = 1
-    rows = 16
-    t0 = time.perf_counter()
-    O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
-    dt = time.perf_counter() - t0
-    rows = int(min(w.M, max(16, rows * seconds / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
-    dt = time.perf_counter() - t0
-    ops = 2.0 * rows * w.N * w.K + 2.0 * rows * w.rank * (w.K + w.N)
-    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(rows / dt, 2),
+    # grow the sample until it takes about `seconds` (whole workload, repeated, if it is smaller)
+    rows, passes, dt = 16, 1, 0.0
+    for _ in range(6):
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * seconds or passes >= 8:
+            break
+        grow = min(8.0, 1.2 * seconds / max(dt, 1e-3))
+        if rows < w.M:
+            rows = int(min(w.M, max(rows + 1, rows * grow)))
+        else:
+            passes = int(min(8, max(passes + 1, passes * grow)))
+    done = rows * passes
+    ops = 2.0 * done * w.N * w.K + 2.0 * done * w.rank * (w.K + w.N)
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(done / dt, 2),
             "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{rows} of {w.M} token rows of {w.name} (full K={w.K}, N={w.N}, r={w.rank}), float64 numpy oracle"}
+            "sample": (f"{rows} of {w.M} token rows of {w.name} x {passes} pass(es) (full K={w.K}, N={w.N}, "
+                       f"r={w.rank}), float64 numpy oracle forward on host cores")}
 
 
 if __name__ == "__main__":

@@ -205,6 +205,33 @@ def test_forward_dit_proj_sampled_rows():
     say(f"dit_proj method error vs X W^T + b: gpu {O.rel_fro(Yg[rows], Yx):.4f} oracle {O.rel_fro(Yref, Yx):.4f}")
 
 
+@pytest.mark.parametrize("name", ["mlp_up", "mlp_down"])
+def test_mlp_linears_full_launch_sampled_rows(name):
+    """The DiT MLP pair's two linears at full size (4608 tokens; 3072 -> 12288 and
+    12288 -> 3072, the down-projection fed GELU_tanh activations): codes and scales
+    bit-exact and Y within tolerance on sampled rows, exact group partials on a block."""
+    say(f"mlp {name}")
+    p = packed(name)
+    d = to_device(p)
+    M, K = p["M"], p["K"]
+    g = synth.rng_for(name, 31)
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(M - 16, M), g.choice(M, 224, replace=False)]))
+    qx, sx, T = run_k1(p, d)
+    qx_o, sx_o, T_o, _ = O.quantize_activations(p["X"][rows], p["s"], p["L1"])
+    np.testing.assert_array_equal(qx[rows], qx_o)
+    np.testing.assert_array_equal(sx[rows].view(np.uint32), sx_o.view(np.uint32))
+    assert O.rel_fro(T[rows], T_o) <= T_REL_FRO
+    Yg = run_forward(p, d)
+    Yref = O.forward(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg[rows], Yref, f"{name} sampled")
+    m0, m1, n0, n1 = M - 40, M, p["N"] - 48, p["N"]
+    qx_full = np.zeros((M, K // 2), np.uint8)
+    qx_blk, _, _, _ = O.quantize_activations(p["X"][m0:m1], p["s"])
+    qx_full[m0:m1] = qx_blk
+    P = run_partials(qx_full, p["Wq"], m0, m1, n0, n1)
+    np.testing.assert_array_equal(P, O.group_partials(qx_blk, p["Wq"][n0:n1]))
+
+
 @pytest.mark.parametrize("M,K,N,r", [(200, 640, 208, 48), (1, 64, 16, 16), (77, 192, 48, 0), (250, 256, 144, 128)])
 def test_forward_ragged_shapes(M, K, N, r):
     """Partial row tiles, partial K stages (K/64 not a multiple of 4), N not a multiple of 128,
@@ -252,3 +279,32 @@ def test_forward_stages_match_fused_call():
     S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], Y, ws, r)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(O.bf16_to_f64(host(Y, np.uint16)), Yf)
+
+
+def test_forward_in_hip_graph_replays_match_eager():
+    """The forward captured in a HIP graph (as the benchmark's graph mode uses it):
+    every replay, with eager work and synchronizations between replays, reproduces
+    the eager output bit for bit."""
+    say("graph replay smallk_1280")
+    p = packed("smallk_1280")
+    d = to_device(p)
+    M, K, N, r = p["M"], p["K"], p["N"], p["r"]
+    Y_eager = run_forward(p, d)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    Yg = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], Yg, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], Yg, ws)
+    for rep in range(3):
+        Yg.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(O.bf16_to_f64(host(Yg, np.uint16)), Y_eager, err_msg=f"replay {rep}")
+        run_forward(p, d)           # eager work between replays
+        torch.cuda.synchronize()
