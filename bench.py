@@ -113,7 +113,7 @@ def main():
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    per_set = (M * K * 2 + M * N * 2 + S.svdq_forward_workspace_bytes(M, K, r)
+    per_set = (M * K * 2 + M * N * 2 + S.svdq_forward_workspace_bytes(M, K, N, r)
                + N * K // 2 + N * K // 64 * 4 + r * (K + N) * 2 + K * 4 + N * 2)
     nsets = max(2, -(-args.rotate_mb * (1 << 20) // per_set))
     sets = []
@@ -122,7 +122,7 @@ def main():
     for i in range(nsets):
         d = {k: v.clone() for k, v in base.items()}
         d["Y"] = torch.empty((M, N), dtype=torch.int16, device=dev)
-        d["work"] = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
+        d["work"] = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=dev)
         sets.append(d)
     torch.cuda.synchronize()
 

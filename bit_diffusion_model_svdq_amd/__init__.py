@@ -55,7 +55,7 @@ _sig = {
     "svdq_act_absmax_update": [_P, ctypes.c_int64, _I, _P],
     "svdq_pack_weights": [_P, _I, _I, _P, ctypes.POINTER(svdq_pack_params), _P, _P, _P, _P, _P, _P],
     "svdq_quantize_residual": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
-    "svdq_forward_workspace_bytes": [_I, _I, _I],
+    "svdq_forward_workspace_bytes": [_I, _I, _I, _I],
     "svdq_linear_forward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_forward_quantize": [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_forward_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -148,8 +148,8 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def svdq_forward_workspace_bytes(M: int, K: int, r: int) -> int:
-    return int(_lib.svdq_forward_workspace_bytes(M, K, r))
+def svdq_forward_workspace_bytes(M: int, K: int, N: int, r: int) -> int:
+    return int(_lib.svdq_forward_workspace_bytes(M, K, N, r))
 
 
 def svdq_linear_forward(X, smooth, L1, L2, Wq, w_scales, bias, Y, workspace, stream=None):

@@ -35,6 +35,8 @@
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // to the 8 XCDs) works on one compact block of tiles, which keeps its share
 // of qx and Wq in its own L2.
+#include <algorithm>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -91,11 +93,8 @@ __device__ inline i32x4 as_i32x4(uint4 v) {
   return r;
 }
 
-// Tile coordinates of this workgroup: XCD-compact, then grouped by 8 token tiles.
-__device__ inline void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
-  const int total = ntm * ntn;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+// Tile coordinates of tile number `id`: rastered in groups of 8 token tiles.
+__device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
   constexpr int GROUP_M = 8;
   const int per_group = GROUP_M * ntn;
   const int grp = id / per_group;
@@ -106,15 +105,31 @@ __device__ inline void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
   tn = in / gsize;
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs; block b of `count` (a
+// multiple of 8) gets tile number (b % 8) * count / 8 + b / 8, so that each
+// XCD works on one compact run of tiles and keeps its qx and Wq rows in its L2.
+__device__ inline int xcd_compact(int b, int count) {
+  return (count & 7) == 0 ? (b & 7) * (count >> 3) + (b >> 3) : b;
+}
+
 // EXPORT = false: the forward.  EXPORT = true: write the group partials P of
 // tokens [row0, row1) x features [col0, col1) instead of the epilogue.
-template <class C, bool EXPORT>
+//
+// Remainder split.  When the tile count leaves a last, nearly empty wave of
+// workgroups, tile numbers [full, full + rem) are cut along K into `splits`
+// shares.  MODE kWhole: block b computes whole tile number b (of `full`).
+// MODE kShares: block u computes share u / rem of tile full + u % rem and
+// stores its raw fp32 accumulators in `part`.  MODE kFixup: block t sums the
+// shares of tile full + t in split order (deterministic) and runs the tail.
+constexpr int kWhole = 0, kShares = 1, kFixup = 2;
+
+template <class C, bool EXPORT, int MODE>
 __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ T,
     int K, int r, const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scales, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ Y, int ldy, int row0, int row1, int col0, int col1,
-    int32_t* __restrict__ P) {
+    int32_t* __restrict__ P, int full, int rem, int splits, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,11 +138,23 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   const int KB = K / 2;
   const int ntm = (row1 - row0 + C::BM - 1) / C::BM;
   const int ntn = (col1 - col0 + C::BN - 1) / C::BN;
+  const int stages = (G + GS - 1) / GS;
   int tmi, tni;
-  tile_of_block(ntm, ntn, tmi, tni);
+  int unit = 0;                       // kShares: slot of this share in `part`
+  int s_begin = 0, s_end = stages;    // kShares: this share's stages
+  if (MODE == kWhole) {
+    tile_of_id(ntm, ntn, xcd_compact(blockIdx.x, full), tmi, tni);
+  } else if (MODE == kFixup) {
+    tile_of_id(ntm, ntn, full + blockIdx.x, tmi, tni);
+  } else {
+    const int tr = blockIdx.x % rem, sp = blockIdx.x / rem;
+    tile_of_id(ntm, ntn, full + tr, tmi, tni);
+    unit = tr * splits + sp;
+    s_begin = (int)((long)stages * sp / splits);
+    s_end = (int)((long)stages * (sp + 1) / splits);
+  }
   const int m0 = row0 + tmi * C::BM;
   const int n0 = col0 + tni * C::BN;
-  const int stages = (G + GS - 1) / GS;
 
   auto stage_a = [&](int buf) { return lds + buf * C::STAGE; };
   auto stage_b = [&](int buf) { return lds + buf * C::STAGE + C::A_BYTES; };
@@ -293,21 +320,69 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     epilogue(dprev, swp, C::TN - 1);
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < stages) gload(s + 1);
-    const int gv = min(GS, G - s * GS);
-#pragma nounroll
-    for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
-    if (s + 1 < stages) sstore(buf ^ 1);
+  if (MODE == kWhole) {
+    gload(0);
+    sstore(0);
     __syncthreads();
+
+    for (int s = 0; s < stages; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < stages) gload(s + 1);
+      const int gv = min(GS, G - s * GS);
+#pragma nounroll
+      for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
+      if (s + 1 < stages) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  } else if (MODE == kShares) {
+    gload(s_begin);
+    sstore(0);
+    __syncthreads();
+
+    for (int s = s_begin; s < s_end; ++s) {
+      const int buf = (s - s_begin) & 1;
+      if (s + 1 < s_end) gload(s + 1);
+      const int gv = min(GS, G - s * GS);
+#pragma nounroll
+      for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
+      if (s + 1 < s_end) sstore(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   if (EXPORT) return;
+
+  // ---- remainder split: store this share, or (FIXUP) sum the shares in order.
+  // Thread-major float4 slots, so every store and load is one contiguous row
+  // of THREADS x 16 bytes.
+  constexpr int NACC = C::TM * C::TN;
+  if (MODE == kShares) {
+    float4* dst = reinterpret_cast<float4*>(part) + (size_t)unit * NACC * C::THREADS + tid;
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const f32x4 a = acc[tm][tn];
+        dst[(size_t)(tm * C::TN + tn) * C::THREADS] = make_float4(a[0], a[1], a[2], a[3]);
+      }
+    return;
+  }
+  if (MODE == kFixup) {
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4* src = reinterpret_cast<const float4*>(part) +
+                          (size_t)(blockIdx.x * splits + sp) * NACC * C::THREADS + tid;
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          const float4 v = src[(size_t)(tm * C::TN + tn) * C::THREADS];
+          acc[tm][tn][0] += v.x;
+          acc[tm][tn][1] += v.y;
+          acc[tm][tn][2] += v.z;
+          acc[tm][tn][3] += v.w;
+        }
+    }
+  }
 
   // ---- epilogue: 1/256, + L2 T^T (bf16 hi/lo MFMA), + bias, bf16 store
 #pragma unroll
@@ -398,60 +473,124 @@ int cu_count() {
   return cached[dev];
 }
 
-template <class C, bool EXPORT>
-hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int K, int r,
-                       const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
-                       const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                       int col1, int32_t* P, hipStream_t stream) {
-  auto kern = w4a4_gemm_kernel<C, EXPORT>;
-  static bool attr_set = false;  // benign race: every caller sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+template <class C, bool EXPORT, int MODE>
+hipError_t set_lds_attr() {
+  static bool done = false;  // benign race: every caller sets the same value
+  if (!done) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(w4a4_gemm_kernel<C, EXPORT, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    done = true;
   }
-  const int tiles = ((row1 - row0 + C::BM - 1) / C::BM) * ((col1 - col0 + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq,
-                     w_scales, bias, Y, ldy, row0, row1, col0, col1, P);
-  return hipGetLastError();
+  return hipSuccess;
+}
+
+template <class C>
+int tiles_of(int rows, int cols) {
+  return ((rows + C::BM - 1) / C::BM) * ((cols + C::BN - 1) / C::BN);
 }
 
 // Tile choice: the biggest tile that still gives every CU at least one workgroup.
 int pick_tile(int rows, int cols) {
   const int cus = cu_count();
-  auto tiles = [&](int bm, int bn) { return ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn); };
-  if (tiles(TileBig::BM, TileBig::BN) >= cus) return 2;
-  if (tiles(TileMed::BM, TileMed::BN) >= cus) return 1;
+  if (tiles_of<TileBig>(rows, cols) >= cus) return 2;
+  if (tiles_of<TileMed>(rows, cols) >= cus) return 1;
   return 0;
+}
+
+// Remainder split of the forward (see the kernel).  Only for the big tile,
+// which holds a whole CU (one workgroup per CU, so the wave of workgroups is
+// `cus` tiles), and only when the last wave is at most a quarter full: then up
+// to 8 K-shares per tile fit in one wave.  A fuller last wave gains less than
+// the shares' partial-sum traffic and the fixup pass cost.
+struct SplitPlan {
+  int full = 0, rem = 0, splits = 1;
+  size_t part_bytes = 0;
+};
+
+template <class C>
+SplitPlan plan_split(int M, int N, int K) {
+  SplitPlan p;
+  const int tiles = tiles_of<C>(M, N);
+  const int cus = cu_count();
+  const int stages = (K / kGroup + GS - 1) / GS;
+  p.full = tiles;
+  const int rem = tiles % cus;
+  if (C::BM * C::BN < TileBig::BM * TileBig::BN || tiles < cus || rem == 0 || 4 * rem > cus)
+    return p;
+  const int splits = std::min(std::min(8, cus / rem), stages);
+  if (splits < 2) return p;
+  p.full = tiles - rem;
+  p.rem = rem;
+  p.splits = splits;
+  p.part_bytes = (size_t)rem * splits * C::BM * C::BN * sizeof(float);
+  return p;
+}
+
+SplitPlan plan_forward(int M, int N, int K) {
+  switch (pick_tile(M, N)) {
+    case 2: return plan_split<TileBig>(M, N, K);
+    case 1: return plan_split<TileMed>(M, N, K);
+    default: return plan_split<TileSmall>(M, N, K);
+  }
+}
+
+template <class C, bool EXPORT>
+hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int K, int r,
+                       const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
+                       const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
+                       int col1, int32_t* P, float* part, hipStream_t stream) {
+  hipError_t e = set_lds_attr<C, EXPORT, kWhole>();
+  if (e != hipSuccess) return e;
+  SplitPlan plan;
+  plan.full = tiles_of<C>(row1 - row0, col1 - col0);
+  if (!EXPORT) plan = plan_split<C>(row1 - row0, col1 - col0, K);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<C, EXPORT, kWhole>), dim3(plan.full), dim3(C::THREADS),
+                     C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
+                     col0, col1, P, plan.full, plan.rem, plan.splits, part);
+  e = hipGetLastError();
+  if (EXPORT || e != hipSuccess || plan.rem == 0) return e;
+  if ((e = set_lds_attr<C, false, kShares>()) != hipSuccess) return e;
+  if ((e = set_lds_attr<C, false, kFixup>()) != hipSuccess) return e;
+  hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kShares>), dim3(plan.rem * plan.splits),
+                     dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
+                     ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kFixup>), dim3(plan.rem), dim3(C::THREADS),
+                     C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
+                     col0, col1, P, plan.full, plan.rem, plan.splits, part);
+  return hipGetLastError();
 }
 
 template <bool EXPORT>
 hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int K, int r,
                     const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                     const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                    int col1, int32_t* P, hipStream_t stream) {
+                    int col1, int32_t* P, float* part, hipStream_t stream) {
   switch (pick_tile(row1 - row0, col1 - col0)) {
     case 2:
       return launch_tile<TileBig, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, stream);
+                                          row1, col0, col1, P, part, stream);
     case 1:
       return launch_tile<TileMed, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, stream);
+                                          row1, col0, col1, P, part, stream);
     default:
       return launch_tile<TileSmall, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                            row1, col0, col1, P, stream);
+                                            row1, col0, col1, P, part, stream);
   }
 }
 
 }  // namespace
 
+size_t gemm_split_bytes(int M, int K, int N) { return plan_forward(M, N, K).part_bytes; }
+
 hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int M, int K,
                             int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
-                            hipStream_t stream) {
+                            float* part, hipStream_t stream) {
   return dispatch<false>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N, nullptr,
-                         stream);
+                         part, stream);
 }
 
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
@@ -459,7 +598,7 @@ hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, in
   (void)M;
   (void)N;
   return dispatch<true>(qx, nullptr, nullptr, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
-                        m1, n0, n1, P, stream);
+                        m1, n0, n1, P, nullptr, stream);
 }
 
 }  // namespace svdq

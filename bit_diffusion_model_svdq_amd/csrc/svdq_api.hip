@@ -24,16 +24,18 @@ svdq_status hip_check(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Workspace carve_workspace(void* base, int M, int K, int r) {
+Workspace carve_workspace(void* base, int M, int K, int N, int r) {
   Workspace w;
   uint8_t* p = static_cast<uint8_t*>(base);
   const size_t qx_bytes = align256((size_t)M * (K / 2));
   const size_t sx_bytes = align256((size_t)M * (K / kGroup) * 4);
   const size_t t_bytes = align256((size_t)M * r * 4);
+  const size_t part_bytes = N > 0 ? align256(gemm_split_bytes(M, K, N)) : 0;
   w.qx = p;
   w.sx = reinterpret_cast<float*>(p + qx_bytes);
   w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
-  w.bytes = qx_bytes + sx_bytes + t_bytes;
+  w.part = part_bytes ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes + t_bytes) : nullptr;
+  w.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
   return w;
 }
 
@@ -104,9 +106,10 @@ svdq_status guarded(F&& f) {
 
 extern "C" {
 
-size_t svdq_forward_workspace_bytes(int M, int K, int r) {
-  if (M < 1 || K < kGroup || K % kGroup || r < 0 || r > kMaxRank || r % 16) return 0;
-  return carve_workspace(nullptr, M, K, r).bytes;
+size_t svdq_forward_workspace_bytes(int M, int K, int N, int r) {
+  if (M < 1 || K < kGroup || K % kGroup || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16)
+    return 0;
+  return carve_workspace(nullptr, M, K, N, r).bytes;
 }
 
 svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const float* smooth,
@@ -116,7 +119,7 @@ svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const 
     SVDQ_TRY(check_shapes(M, K, 16, r, false));
     SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
     SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const Workspace w = carve_workspace(workspace, M, K, r);
+    const Workspace w = carve_workspace(workspace, M, K, 0, r);   // stage 1 needs no partials
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
@@ -132,11 +135,11 @@ svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, co
     SVDQ_TRY(check_shapes(M, K, N, r, true));
     SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
     SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, r);
+    const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, N, r);
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y,
-                                      static_cast<hipStream_t>(stream)),
+                                      w.part, static_cast<hipStream_t>(stream)),
                      "w4a4_gemm launch");
   });
 }
@@ -152,14 +155,14 @@ svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
     SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
     SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
     SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const Workspace w = carve_workspace(workspace, M, K, r);
+    const Workspace w = carve_workspace(workspace, M, K, N, r);
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, s),
                        "smooth_quant_lora_down launch"));
     return hip_check(
-        launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y, s),
+        launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y, w.part, s),
         "w4a4_gemm launch");
   });
 }

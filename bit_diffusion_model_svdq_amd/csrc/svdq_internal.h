@@ -15,14 +15,20 @@ constexpr int kMaxRank = 128;   // rank bound of the low-rank branch
 
 svdq_status hip_check(hipError_t e, const char* what);
 
-// Workspace carving: qx [M, K/2] | sx [M, K/64] | T [M, r], each 256-byte aligned.
+// Workspace carving: qx [M, K/2] | sx [M, K/64] | T [M, r] | split partials
+// (only when k2 splits a last partial wave of tiles; N = 0 leaves them out),
+// each part 256-byte aligned.
 struct Workspace {
   uint8_t* qx;
   float* sx;
   float* T;
+  float* part;
   size_t bytes;
 };
-Workspace carve_workspace(void* base, int M, int K, int r);
+Workspace carve_workspace(void* base, int M, int K, int N, int r);
+
+// Bytes of fp32 partial accumulators k2 needs for an M x N x K forward.
+size_t gemm_split_bytes(int M, int K, int N);
 
 // k1: x_hat = X * (1/s); per-64 absmax, scales and codes; T = x_hat L1^T.
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
@@ -33,7 +39,7 @@ hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
 hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int M, int K,
                             int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
-                            hipStream_t stream);
+                            float* part, hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

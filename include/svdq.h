@@ -105,15 +105,19 @@ svdq_status svdq_quantize_residual(const float* W, int N, int K, const float* sm
 
 /* ---------------------------------------------------------------- device */
 
-/* Workspace the forward needs: qx, sx and T, each part 256-byte aligned. */
-size_t svdq_forward_workspace_bytes(int M, int K, int r);
+/* Workspace the forward needs, in bytes: the activation codes qx, their
+ * scales sx and T = x_hat L1^T, plus fp32 partial accumulators when the GEMM
+ * cuts a last, partial wave of output tiles along K (this part depends on N
+ * and on the current device's compute-unit count).  Each part is 256-byte
+ * aligned.  Returns 0 for shapes the forward rejects. */
+size_t svdq_forward_workspace_bytes(int M, int K, int N, int r);
 
 /* The SVDQuant linear forward (E4): launches the fused smooth + quantize +
  * lora_down kernel, then the W4A4 GEMM whose epilogue applies the group
  * scales, adds the lora_up product and the bias and stores bf16 Y.
  * Requires M >= 1, K % 64 == 0, N % 16 == 0, 0 <= r <= 128, r % 16 == 0,
  * 16-byte aligned device pointers (bias and, for r = 0, L1/L2 may be NULL)
- * and workspace_bytes >= svdq_forward_workspace_bytes(M, K, r).  Asynchronous
+ * and workspace_bytes >= svdq_forward_workspace_bytes(M, K, N, r).  Asynchronous
  * on `stream`; no allocation, no synchronization. */
 svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
                                 const float* smooth, const uint16_t* L1, const uint16_t* L2,

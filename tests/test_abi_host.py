@@ -158,12 +158,18 @@ def test_pack_rejects_bad_arguments_and_writes_nothing():
 
 
 def test_workspace_bytes():
-    M, K, r = 4096, 3072, 32
-    b = S.svdq_forward_workspace_bytes(M, K, r)
+    """qx + sx + T; plus the GEMM's split partials when its 256 x 192 tiles leave a
+    last partial wave (this container has no GPU: the library assumes 256 CUs)."""
     al = lambda x: (x + 255) // 256 * 256
+    M, K, N, r = 4096, 3072, 3072, 32          # 16 x 16 = 256 tiles: one full wave
+    b = S.svdq_forward_workspace_bytes(M, K, N, r)
     assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(M * r * 4)
-    assert S.svdq_forward_workspace_bytes(M, 100, r) == 0
-    assert S.svdq_forward_workspace_bytes(M, K, 24) == 0
+    M, K, N = 4608, 12288, 3072                # 18 x 16 = 288 tiles: 32 left, each cut 8 ways
+    b = S.svdq_forward_workspace_bytes(M, K, N, r)
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(M * r * 4) + 32 * 8 * 256 * 192 * 4
+    assert S.svdq_forward_workspace_bytes(M, 100, N, r) == 0
+    assert S.svdq_forward_workspace_bytes(M, K, 40, r) == 0
+    assert S.svdq_forward_workspace_bytes(M, K, N, 24) == 0
 
 
 def test_device_entry_points_validate_before_launching():
@@ -171,7 +177,7 @@ def test_device_entry_points_validate_before_launching():
     L = S._lib
     a = 1 << 20            # a fake 16-byte-aligned address; never dereferenced
     mis = a + 4
-    ws = S.svdq_forward_workspace_bytes(256, 1024, 16)
+    ws = S.svdq_forward_workspace_bytes(256, 1024, 1024, 16)
     fwd = lambda X=a, M=256, K=1024, N=1024, r=16, L1=a, L2=a, bias=a, wsb=ws: L.svdq_linear_forward(
         X, M, K, N, r, a, L1, L2, a, a, bias, a, a, wsb, None)
     assert fwd(K=1000) == 1

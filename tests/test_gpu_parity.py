@@ -90,7 +90,7 @@ def run_k1(p, d):
 def run_forward(p, d, with_bias=True):
     M, K, N, r = p["M"], p["K"], p["N"], p["r"]
     Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
-    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=DEV)
     S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"] if with_bias else None,
                           Y, ws)
     torch.cuda.synchronize()
@@ -232,6 +232,28 @@ def test_mlp_linears_full_launch_sampled_rows(name):
     np.testing.assert_array_equal(P, O.group_partials(qx_blk, p["Wq"][n0:n1]))
 
 
+def test_forward_remainder_split_ragged():
+    """4300 x 256 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192, so 16 tiles
+    (including the ragged last token tile) are cut along K into as many shares as
+    there are stages (2) and summed by the fixup pass."""
+    say("forward remainder split 4300x256x3072 r=48")
+    w = synth.WORKLOADS["dit_proj"]
+    M, K, N, r = 4300, 256, 3072, 48
+    X = np.ascontiguousarray(synth.activations(w, M)[:, :K])
+    W = np.ascontiguousarray(synth.weight(w)[:N, :K])
+    b = synth.bias(w)[:N]
+    A = O.act_absmax(synth.calibration_activations(w)[:, :K])
+    pk = O.pack_weights(W, A, 0.5, rank=r)
+    p = dict(X=X, b=b, r=r, M=M, K=K, N=N, s=pk["s"], L1=pk["L1"], L2=pk["L2"], Wq=pk["Wq"],
+             w_scales=pk["w_scales"])
+    d = to_device(p)
+    Yg = run_forward(p, d)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(3840, 3856), np.arange(M - 40, M),
+                                     synth.rng_for("dit_proj", 32).choice(M, 200, replace=False)]))
+    Yref = O.forward(X[rows], pk["s"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+    check_y(Yg[rows], Yref, "remainder split")
+
+
 @pytest.mark.parametrize("M,K,N,r", [(200, 640, 208, 48), (1, 64, 16, 16), (77, 192, 48, 0), (250, 256, 144, 128)])
 def test_forward_ragged_shapes(M, K, N, r):
     """Partial row tiles, partial K stages (K/64 not a multiple of 4), N not a multiple of 128,
@@ -273,7 +295,7 @@ def test_forward_stages_match_fused_call():
     d = to_device(p)
     Yf = run_forward(p, d)
     M, K, N, r = p["M"], p["K"], p["N"], p["r"]
-    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=DEV)
     Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
     S.svdq_forward_quantize(d["X"], d["s"], d["L1"], ws)
     S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], Y, ws, r)
@@ -290,7 +312,7 @@ def test_forward_in_hip_graph_replays_match_eager():
     d = to_device(p)
     M, K, N, r = p["M"], p["K"], p["N"], p["r"]
     Y_eager = run_forward(p, d)
-    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=DEV)
     Yg = torch.empty((M, N), dtype=torch.int16, device=DEV)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
