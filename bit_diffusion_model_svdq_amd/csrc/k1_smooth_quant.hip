@@ -8,38 +8,50 @@
 // running the low-rank branch as a separate kernel re-reads the activations.
 // Here X is read from HBM exactly once.
 //
-// Work split: one workgroup owns 16 rows (one MFMA row tile) and all of K;
-// each of its 8 waves takes a contiguous run of 64-channel groups and issues
-// the loads of up to 6 groups at once (the whole run for K <= 3072), so
-// that a workgroup has its entire slice of X in flight.  Lane
-// l holds row (l % 16) and, of each group, channels 8 * (l / 16) + 0..7 and
-// 32 + 8 * (l / 16) + 0..7: exactly the A operand layout of two 16x16x32 bf16
-// MFMAs, and two 16-byte loads that cover 64 contiguous bytes per row.  The
-// group absmax is a local max plus two cross-lane steps.
+// Work split.  A workgroup owns RTM row tiles of 16 rows and one slice of K
+// (grid.y = slices); its 8 waves split the slice's 64-channel groups into
+// contiguous runs.  A wave handles all RTM row tiles of each of its groups,
+// so every lora_down fragment it loads serves RTM row tiles: L1 is read from
+// L2 once per 16 * RTM rows.  Slices keep >= 256 workgroups when RTM row tiles
+// per block leave too few; each slice writes its own partial T (slice-major,
+// [slices][M][r]) and the GEMM kernel sums the slices in order when it loads T.
 //
+// Loads.  Lane l holds row (l % 16) of a tile and, of each group, channels
+// 8 * (l / 16) + 0..7 and 32 + 8 * (l / 16) + 0..7: exactly the A operand of
+// two 16x16x32 bf16 MFMAs, in two 16-byte loads that cover 64 contiguous bytes
+// per row.  The groups of a run go through a window of CH register slots: the
+// loads of group g + CH are issued as soon as group g is processed, before
+// group g's codes are stored (the vector-memory counter retires in order, so
+// a store ahead of a load would make that load's consumer wait for the store).
+// Loads are branch-free: rows past M and groups past the run re-read valid
+// data that is never used.
+//
+// Quantization.  The group absmax is a local max plus two cross-lane steps.
 // Rounding to the integer code uses the float32 adder: for |y| <= 7.0000005,
-// fl32(y + 1.5 * 2^23) = 1.5 * 2^23 + rne(y) exactly, so the low byte of its
-// bit pattern is the code as an int8 and its low nibble is the packed code.
-// |y| cannot exceed 7 * (1 + 2^-24) because inv = fl32(7 / amax), so no clamp
-// is needed.  x_hat enters the MFMA as a bf16 hi/lo pair (hi = x_hat with the
+// fl32(y + 1.5 * 2^23) = 1.5 * 2^23 + rne(y) exactly, so the low nibble of its
+// bit pattern is the packed code.  |y| cannot exceed 7 * (1 + 2^-24) because
+// inv = fl32(7 / amax), so no clamp is needed.
+//
+// lora_down.  x_hat enters the MFMA as a bf16 hi/lo pair (hi = x_hat with the
 // low 16 bits cleared, lo = bf16(x_hat - hi), an exact difference), so T keeps
-// ~16 significant bits.  The 8 waves' T partials are summed in LDS in a fixed
+// ~16 significant bits.  The waves' partial T are summed in LDS in a fixed
 // order (deterministic).
+#include <algorithm>
+
 #include "svdq_internal.h"
 
 namespace svdq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 8;
-constexpr int kRows = 16;
-constexpr int kThreads = kWaves * 64;
-constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kW = 8;                  // waves per workgroup
+constexpr int kThreads = kW * 64;
+constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+constexpr size_t kLdsBudget = 152 * 1024;
 
 __device__ inline uint32_t cvt_bf16x2(float a, float b) {  // round-to-nearest-even pair
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
@@ -63,46 +75,92 @@ __device__ inline uint32_t pack8(const float* z) {  // 8 codes -> one dword
   return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
 }
 
-template <int RT>  // RT = r / 16 column tiles of T
+// groups in flight per wave: about 100 VGPRs of loaded data
+template <int RT, int RTM>
+constexpr int window() {
+  constexpr int per_group = 8 * RTM + 8 * RT;
+  constexpr int w = 100 / per_group;
+  return w < 1 ? 1 : (w > 6 ? 6 : w);
+}
+
+// RT = r / 16 rank tiles; RTM row tiles per workgroup; gslice groups per K-slice.
+template <int RT, int RTM>
 __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, float* __restrict__ sx,
-    float* __restrict__ T) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // inv_s [K] | T partials [kWaves][16][r]
-  float* inv_s = lds;
-  float* tpart = lds + K;
-
+    float* __restrict__ T, int gslice) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // inv_s [gslice*64] | T partials
+  constexpr int NL = RT > 0 ? 2 * RT : 1;
+  constexpr int CH = window<RT, RTM>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int m0 = blockIdx.x * kRows;
   const int G = K / kGroup;
-  const int per_wave = (G + kWaves - 1) / kWaves;
-  const int g_begin = min(G, wave * per_wave);
-  const int g_end = min(G, g_begin + per_wave);
+  const int slice = blockIdx.y;
+  const int sg0 = slice * gslice;                 // first group of the slice
+  const int sg1 = min(G, sg0 + gslice);
+  const int per_wave = (sg1 - sg0 + kW - 1) / kW;
+  const int g_begin = min(sg1, sg0 + wave * per_wave);
+  const int g_end = min(sg1, g_begin + per_wave);
+  const int g_last = max(g_end - 1, sg0);         // a wave without groups re-reads a valid one
+  float* inv_s = lds;                             // channels of the slice
+  float* tpart = lds + gslice * kGroup;
 
-  // fl32(1 / s[k]): IEEE division, once per workgroup.
-  for (int k = tid; k < K; k += kThreads) inv_s[k] = 1.0f / smooth[k];
-
-  const int row = m0 + (lane & 15);
-  const bool row_ok = row < M;
+  const int m0 = blockIdx.x * 16 * RTM;
+  const int fr = lane & 15;
   const int fk = lane >> 4;
-  // rows past M read row M-1 (never stored): every load is unconditional, so
-  // the compiler issues them back to back instead of draining at branch joins
-  const uint16_t* xrow = X + (size_t)min(row, M - 1) * K + 8 * fk;
-  f32x4 acc[RT > 0 ? RT : 1];
+  const uint16_t* xrow[RTM];
 #pragma unroll
-  for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RTM; ++t) xrow[t] = X + (size_t)min(m0 + 16 * t + fr, M - 1) * K + 8 * fk;
+  const uint16_t* l1row = L1 + (size_t)fr * K + 8 * fk;
+
+  uint4 xa[CH][RTM], xb[CH][RTM], lb[CH][NL];
+  auto load_group = [&](int slot, int g) {
+    const int gg = min(g, g_last);
+#pragma unroll
+    for (int t = 0; t < RTM; ++t) {
+      xa[slot][t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup);
+      xb[slot][t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup + 32);
+    }
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int j = 0; j < RT; ++j) {
+        const uint16_t* lp = l1row + (size_t)j * 16 * K + gg * kGroup;
+        lb[slot][2 * j] = *reinterpret_cast<const uint4*>(lp);
+        lb[slot][2 * j + 1] = *reinterpret_cast<const uint4*>(lp + 32);
+      }
+    }
+  };
+
+  // fl32(1 / s[k]) for the slice, IEEE division, once per workgroup.  The
+  // first kPre values per thread are requested before the first groups, so
+  // that the barrier below does not wait for them; everything up to the
+  // barrier is branch-free (clamped indices, duplicates store equal values).
+  constexpr int kPre = 4;
+  const int c0 = sg0 * kGroup, nc = (sg1 - sg0) * kGroup;
+  float sv[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) sv[i] = smooth[c0 + min(tid + i * kThreads, nc - 1)];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) load_group(j, g_begin + j);
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) inv_s[min(tid + i * kThreads, nc - 1)] = 1.0f / sv[i];
+  if (nc > kPre * kThreads)
+    for (int k = tid + kPre * kThreads; k < nc; k += kThreads) inv_s[k] = 1.0f / smooth[c0 + k];
+
+  f32x4 acc[RTM][RT > 0 ? RT : 1];
+#pragma unroll
+  for (int t = 0; t < RTM; ++t)
+#pragma unroll
+    for (int j = 0; j < (RT > 0 ? RT : 1); ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();  // inv_s ready
 
-  // Process one group whose X pieces (xa: channels 8fk..+7, xb: 32+8fk..+7) are in registers.
-  // The codes and the scale come back in registers: stores share the in-order
-  // vector-memory counter with loads, so a store issued here would make the
-  // next group's wait for its prefetched L1 fragments wait for the store too.
-  auto process = [&](int g, uint4 xa, uint4 xb, const uint4* lb, uint2& out, float& out_scale) {
-    const int k0 = g * kGroup + 8 * fk;
-    const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+  // One group of one row tile from registers: codes, scale, and the lora_down MFMAs.
+  auto process = [&](int g, uint4 va, uint4 vb, const uint4* lf, f32x4* at, uint2& codes,
+                     float& scale) {
+    const int k0 = (g - sg0) * kGroup + 8 * fk;
+    const uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
     float xh[16];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -120,14 +178,13 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float scale = amax / 7.0f;
+    scale = amax / 7.0f;
     const float inv = amax > 0.f ? 7.0f / amax : 0.f;
     float z[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
-    out.x = pack8(z);
-    out.y = pack8(z + 8);
-    out_scale = scale;
+    codes.x = pack8(z);
+    codes.y = pack8(z + 8);
     if constexpr (RT > 0) {
       uint32_t hi[8], lo[8];
 #pragma unroll
@@ -142,116 +199,145 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       const bf16x8 alo0 = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
       const bf16x8 alo1 = as_bf16x8(make_uint4(lo[4], lo[5], lo[6], lo[7]));
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const bf16x8 b0 = as_bf16x8(lb[2 * t]), b1 = as_bf16x8(lb[2 * t + 1]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi0, b0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo0, b0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi1, b1, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo1, b1, acc[t], 0, 0, 0);
-      }
-    }
-  };
-  constexpr int NL = RT > 0 ? 2 * RT : 1;
-  constexpr int kChunk = RT > 4 ? 3 : 6;  // groups whose X loads are in flight together
-  auto load_l1 = [&](int g, uint4* lb) {
-    if constexpr (RT > 0) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const uint16_t* lp = L1 + (size_t)(t * 16 + (lane & 15)) * K + g * kGroup + 8 * fk;
-        lb[2 * t] = *reinterpret_cast<const uint4*>(lp);
-        lb[2 * t + 1] = *reinterpret_cast<const uint4*>(lp + 32);
+      for (int j = 0; j < RT; ++j) {
+        const bf16x8 b0 = as_bf16x8(lf[2 * j]), b1 = as_bf16x8(lf[2 * j + 1]);
+        at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi0, b0, at[j], 0, 0, 0);
+        at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo0, b0, at[j], 0, 0, 0);
+        at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi1, b1, at[j], 0, 0, 0);
+        at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo1, b1, at[j], 0, 0, 0);
       }
     }
   };
 
-  for (int c0 = g_begin; c0 < g_end; c0 += kChunk) {
-    // all X loads of the chunk first
-    uint4 xa[kChunk], xb[kChunk];
+  auto store_group = [&](int g, const uint2* codes, const float* scales) {
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const int gj = min(c0 + j, g_end - 1);   // groups past the run re-read its last one (unused)
-      xa[j] = *reinterpret_cast<const uint4*>(xrow + gj * kGroup);
-      xb[j] = *reinterpret_cast<const uint4*>(xrow + gj * kGroup + 32);
-    }
-    uint4 lbc[NL], lbn[NL];
-#pragma unroll
-    for (int e = 0; e < NL; ++e) lbn[e] = make_uint4(0u, 0u, 0u, 0u);
-    load_l1(c0, lbc);
-    uint2 codes[kChunk];
-    float scales[kChunk];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      codes[j] = make_uint2(0u, 0u);
-      scales[j] = 0.f;
-      if (c0 + j < g_end) {
-        if (j + 1 < kChunk && c0 + j + 1 < g_end) load_l1(c0 + j + 1, lbn);
-        process(c0 + j, xa[j], xb[j], lbc, codes[j], scales[j]);
-#pragma unroll
-        for (int e = 0; e < NL; ++e) lbc[e] = lbn[e];
+    for (int t = 0; t < RTM; ++t) {
+      const int row = m0 + 16 * t + fr;
+      if (row < M) {
+        uint8_t* qrow = qx + (size_t)row * (K / 2) + g * 32 + 4 * fk;
+        *reinterpret_cast<uint32_t*>(qrow) = codes[t].x;
+        *reinterpret_cast<uint32_t*>(qrow + 16) = codes[t].y;
+        if (fk == 0) sx[(size_t)row * G + g] = scales[t];
       }
     }
-    if (row_ok) {
+  };
+  // Whole windows: process a slot, refill it with the group CH ahead, then
+  // store.  The refill is unconditional (clamped) so that the loop body has no
+  // branch around a load: at a branch join the compiler would have to assume
+  // the worst and wait for every load in flight.
+  int gb = g_begin;
+  for (; gb + CH <= g_end; gb += CH) {
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        if (c0 + j < g_end) {
-          uint8_t* qrow = qx + (size_t)row * (K / 2) + (c0 + j) * 32 + 4 * fk;
-          *reinterpret_cast<uint32_t*>(qrow) = codes[j].x;
-          *reinterpret_cast<uint32_t*>(qrow + 16) = codes[j].y;
-          if (fk == 0) sx[(size_t)row * G + c0 + j] = scales[j];
-        }
-      }
+    for (int j = 0; j < CH; ++j) {
+      uint2 codes[RTM];
+      float scales[RTM];
+#pragma unroll
+      for (int t = 0; t < RTM; ++t)
+        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
+      load_group(j, gb + j + CH);
+      store_group(gb + j, codes, scales);
+    }
+  }
+  // The last, partial window is already in slots 0 .. g_end - gb - 1.
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if (gb + j < g_end) {
+      uint2 codes[RTM];
+      float scales[RTM];
+#pragma unroll
+      for (int t = 0; t < RTM; ++t)
+        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
+      store_group(gb + j, codes, scales);
     }
   }
 
   if constexpr (RT > 0) {
     // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + i.
+    // Partials [wave][row of the block][rank], summed over waves in order.
+    constexpr int RB = 16 * RTM;
+    float* Ts = T + (size_t)slice * M * r;
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < RTM; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tpart[(wave * 16 + 4 * fk + i) * r + t * 16 + (lane & 15)] = acc[t][i];
+      for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tpart[(wave * RB + 16 * t + 4 * fk + i) * r + 16 * j + fr] = acc[t][j][i];
     __syncthreads();
-    for (int e = tid; e < 16 * r; e += kThreads) {
+    for (int e = tid; e < RB * r; e += kThreads) {
       const int rr = e / r, c = e - (e / r) * r;
       float s = 0.f;
 #pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) s += tpart[(wv * 16 + rr) * r + c];
-      if (m0 + rr < M) T[(size_t)(m0 + rr) * r + c] = s;
+      for (int wv = 0; wv < kW; ++wv) s += tpart[(wv * RB + rr) * r + c];
+      if (m0 + rr < M) Ts[(size_t)(m0 + rr) * r + c] = s;
     }
   }
 }
 
-template <int RT>
-hipError_t launch_rt(const uint16_t* X, int M, int K, int r, const float* smooth,
-                     const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
-  const size_t lds = (size_t)K * 4 + (size_t)kWaves * 16 * r * 4;
-  auto kern = smooth_quant_lora_down_kernel<RT>;
+size_t lds_bytes(int rtm, int gslice, int r) {
+  return (size_t)gslice * kGroup * 4 + (size_t)kW * 16 * rtm * r * 4;
+}
+
+template <int RT, int RTM>
+hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
+                  const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
+  const size_t lds = lds_bytes(RTM, p.gslice, r);
+  auto kern = smooth_quant_lora_down_kernel<RT, RTM>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int blocks = (M + kRows - 1) / kRows;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, X, M, K, smooth, L1, r, qx,
-                     sx, T);
+  const int rb = (M + 16 * RTM - 1) / (16 * RTM);
+  hipLaunchKernelGGL(kern, dim3(rb, p.slices), dim3(kThreads), lds, stream, X, M, K, smooth, L1,
+                     r, qx, sx, T, p.gslice);
   return hipGetLastError();
+}
+
+template <int RT>
+hipError_t launch_rt(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
+                     const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
+  if (p.rtm == 2) return launch<RT, 2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+  return launch<RT, 1>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
 }
 
 }  // namespace
 
+// Row tiles per workgroup and K-slices.  Two row tiles halve the L1 traffic
+// (worth it with a low-rank branch and enough rows); slices then restore
+// >= 256 workgroups, keeping >= 8 groups (one per wave) per slice, and are
+// added while the slice's LDS does not fit.
+K1Plan k1_plan(int M, int K, int r, bool one_slice) {
+  K1Plan p;
+  const int G = K / kGroup;
+  p.rtm = (r > 0 && M >= 2048) ? 2 : 1;
+  int slices = 1;
+  if (one_slice) {
+    if (lds_bytes(p.rtm, G, r) > kLdsBudget) p.rtm = 1;
+  } else {
+    const int rb = (M + 16 * p.rtm - 1) / (16 * p.rtm);
+    slices = std::max(1, std::min((256 + rb - 1) / rb, G / kW));
+    while (slices < G && lds_bytes(p.rtm, (G + slices - 1) / slices, r) > kLdsBudget) ++slices;
+  }
+  p.gslice = (G + slices - 1) / slices;
+  p.slices = (G + p.gslice - 1) / p.gslice;
+  return p;
+}
+
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
-                                         float* sx, float* T, hipStream_t stream) {
+                                         float* sx, float* T, bool one_slice, hipStream_t stream) {
+  const K1Plan p = k1_plan(M, K, r, one_slice);
   switch (r / 16) {
-    case 0: return launch_rt<0>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 1: return launch_rt<1>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 2: return launch_rt<2>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 3: return launch_rt<3>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 4: return launch_rt<4>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 5: return launch_rt<5>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 6: return launch_rt<6>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 7: return launch_rt<7>(X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 8: return launch_rt<8>(X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 0: return launch_rt<0>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 1: return launch_rt<1>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 2: return launch_rt<2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 3: return launch_rt<3>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 4: return launch_rt<4>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 5: return launch_rt<5>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 6: return launch_rt<6>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 7: return launch_rt<7>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 8: return launch_rt<8>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
     default: return hipErrorInvalidValue;
   }
 }

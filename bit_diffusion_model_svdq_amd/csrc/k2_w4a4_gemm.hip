@@ -129,7 +129,8 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     int K, int r, const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scales, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ Y, int ldy, int row0, int row1, int col0, int col1,
-    int32_t* __restrict__ P, int full, int rem, int splits, float* __restrict__ part) {
+    int32_t* __restrict__ P, int full, int rem, int splits, float* __restrict__ part,
+    int t_slices, long t_stride) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -401,8 +402,17 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       const int m = m0 + wr + 16 * t + fr;
       float tv[8];
       if (j_ok && m < row1) {
-        const float4* tp = reinterpret_cast<const float4*>(T + (size_t)m * r + j);
-        const float4 a = tp[0], b = tp[1];
+        // T arrives as t_slices partial sums (one per K-slice of the quantize
+        // kernel), added here in slice order
+        const float* tp = T + (size_t)m * r + j;
+        float4 a = *reinterpret_cast<const float4*>(tp);
+        float4 b = *reinterpret_cast<const float4*>(tp + 4);
+        for (int sl = 1; sl < t_slices; ++sl) {
+          const float4 a2 = *reinterpret_cast<const float4*>(tp + sl * t_stride);
+          const float4 b2 = *reinterpret_cast<const float4*>(tp + sl * t_stride + 4);
+          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+          b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+        }
         tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
         tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
       } else {
@@ -537,7 +547,7 @@ SplitPlan plan_forward(int M, int N, int K) {
 }
 
 template <class C, bool EXPORT>
-hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int K, int r,
+hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                        const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                        const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
                        int col1, int32_t* P, float* part, hipStream_t stream) {
@@ -548,35 +558,38 @@ hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int K
   if (!EXPORT) plan = plan_split<C>(row1 - row0, col1 - col0, K);
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, EXPORT, kWhole>), dim3(plan.full), dim3(C::THREADS),
                      C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
-                     col0, col1, P, plan.full, plan.rem, plan.splits, part);
+                     col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
+                     (long)(row1 - row0) * r);
   e = hipGetLastError();
   if (EXPORT || e != hipSuccess || plan.rem == 0) return e;
   if ((e = set_lds_attr<C, false, kShares>()) != hipSuccess) return e;
   if ((e = set_lds_attr<C, false, kFixup>()) != hipSuccess) return e;
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kShares>), dim3(plan.rem * plan.splits),
                      dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
-                     ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part);
+                     ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part,
+                     t_slices, (long)(row1 - row0) * r);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kFixup>), dim3(plan.rem), dim3(C::THREADS),
                      C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
-                     col0, col1, P, plan.full, plan.rem, plan.splits, part);
+                     col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
+                     (long)(row1 - row0) * r);
   return hipGetLastError();
 }
 
 template <bool EXPORT>
-hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int K, int r,
+hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                     const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                     const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
                     int col1, int32_t* P, float* part, hipStream_t stream) {
   switch (pick_tile(row1 - row0, col1 - col0)) {
     case 2:
-      return launch_tile<TileBig, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+      return launch_tile<TileBig, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
                                           row1, col0, col1, P, part, stream);
     case 1:
-      return launch_tile<TileMed, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+      return launch_tile<TileMed, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
                                           row1, col0, col1, P, part, stream);
     default:
-      return launch_tile<TileSmall, EXPORT>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
+      return launch_tile<TileSmall, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
                                             row1, col0, col1, P, part, stream);
   }
 }
@@ -585,19 +598,19 @@ hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int K, i
 
 size_t gemm_split_bytes(int M, int K, int N) { return plan_forward(M, N, K).part_bytes; }
 
-hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int M, int K,
-                            int N, int r, const uint16_t* L2, const uint8_t* Wq,
+hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int t_slices,
+                            int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
                             float* part, hipStream_t stream) {
-  return dispatch<false>(qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N, nullptr,
-                         part, stream);
+  return dispatch<false>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N,
+                         nullptr, part, stream);
 }
 
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                  int m0, int m1, int n0, int n1, int32_t* P, hipStream_t stream) {
   (void)M;
   (void)N;
-  return dispatch<true>(qx, nullptr, nullptr, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
+  return dispatch<true>(qx, nullptr, nullptr, 0, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
                         m1, n0, n1, P, nullptr, stream);
 }
 

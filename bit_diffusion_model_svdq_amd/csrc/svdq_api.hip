@@ -29,7 +29,8 @@ Workspace carve_workspace(void* base, int M, int K, int N, int r) {
   uint8_t* p = static_cast<uint8_t*>(base);
   const size_t qx_bytes = align256((size_t)M * (K / 2));
   const size_t sx_bytes = align256((size_t)M * (K / kGroup) * 4);
-  const size_t t_bytes = align256((size_t)M * r * 4);
+  w.t_slices = k1_plan(M, K, r, false).slices;
+  const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
   const size_t part_bytes = N > 0 ? align256(gemm_split_bytes(M, K, N)) : 0;
   w.qx = p;
   w.sx = reinterpret_cast<float*>(p + qx_bytes);
@@ -122,7 +123,7 @@ svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const 
     const Workspace w = carve_workspace(workspace, M, K, 0, r);   // stage 1 needs no partials
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
+    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, false,
                                                    static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down launch");
   });
@@ -138,8 +139,8 @@ svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, co
     const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, N, r);
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y,
-                                      w.part, static_cast<hipStream_t>(stream)),
+    return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales,
+                                      bias, Y, w.part, static_cast<hipStream_t>(stream)),
                      "w4a4_gemm launch");
   });
 }
@@ -159,10 +160,11 @@ svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, s),
+    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, false, s),
                        "smooth_quant_lora_down launch"));
     return hip_check(
-        launch_w4a4_gemm(w.qx, w.sx, w.T, M, K, N, r, L2, Wq, w_scales, bias, Y, w.part, s),
+        launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales, bias, Y, w.part,
+                         s),
         "w4a4_gemm launch");
   });
 }
@@ -176,7 +178,7 @@ svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const flo
     SVDQ_TRY(check_ptr(qx, "qx", false));
     SVDQ_TRY(check_ptr(sx, "sx", false));
     SVDQ_TRY(check_ptr(T, "T", r == 0));
-    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, qx, sx, T,
+    return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, qx, sx, T, true,
                                                    static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down launch");
   });

@@ -15,13 +15,14 @@ constexpr int kMaxRank = 128;   // rank bound of the low-rank branch
 
 svdq_status hip_check(hipError_t e, const char* what);
 
-// Workspace carving: qx [M, K/2] | sx [M, K/64] | T [M, r] | split partials
+// Workspace carving: qx [M, K/2] | sx [M, K/64] | T [slices, M, r] | split partials
 // (only when k2 splits a last partial wave of tiles; N = 0 leaves them out),
 // each part 256-byte aligned.
 struct Workspace {
   uint8_t* qx;
   float* sx;
-  float* T;
+  float* T;         // t_slices x M x r partial sums of x_hat L1^T
+  int t_slices;
   float* part;
   size_t bytes;
 };
@@ -31,13 +32,22 @@ Workspace carve_workspace(void* base, int M, int K, int N, int r);
 size_t gemm_split_bytes(int M, int K, int N);
 
 // k1: x_hat = X * (1/s); per-64 absmax, scales and codes; T = x_hat L1^T.
+// The launch shape: rtm row tiles of 16 per workgroup, K cut into `slices`
+// slices of gslice groups; each slice writes its own partial T, so T holds
+// slices x M x r floats (slice-major).  one_slice asks for a single slice,
+// i.e. T itself.
+struct K1Plan {
+  int rtm = 1, slices = 1, gslice = 1;
+};
+K1Plan k1_plan(int M, int K, int r, bool one_slice);
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
-                                         float* sx, float* T, hipStream_t stream);
+                                         float* sx, float* T, bool one_slice, hipStream_t stream);
 
-// k2: Y = sum_g sx sw P_g + T L2^T + b, bf16 out.
-hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int M, int K,
-                            int N, int r, const uint16_t* L2, const uint8_t* Wq,
+// k2: Y = sum_g sx sw P_g + T L2^T + b, bf16 out.  T holds t_slices partial
+// sums of M x r floats, added in order.
+hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int t_slices,
+                            int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
                             float* part, hipStream_t stream);
 
