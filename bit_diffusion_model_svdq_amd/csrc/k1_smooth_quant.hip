@@ -20,11 +20,16 @@
 // 8 * (l / 16) + 0..7 and 32 + 8 * (l / 16) + 0..7: exactly the A operand of
 // two 16x16x32 bf16 MFMAs, in two 16-byte loads that cover 64 contiguous bytes
 // per row.  The groups of a run go through a window of CH register slots: the
-// loads of group g + CH are issued as soon as group g is processed, before
-// group g's codes are stored (the vector-memory counter retires in order, so
-// a store ahead of a load would make that load's consumer wait for the store).
-// Loads are branch-free: rows past M and groups past the run re-read valid
-// data that is never used.
+// loads of group g + CH are issued as soon as group g is processed.  A small
+// window measured faster than a deep one: with every wave of the chip asking
+// for its whole run at once, each wave's first group comes back late.  Loads
+// are branch-free: rows past M and groups past the run re-read valid data
+// that is never used.
+//
+// Stores.  Codes and scales are collected in LDS and leave at the end as whole
+// row segments of the slice (16-byte stores), so no store shares the in-order
+// vector-memory counter with a load still to be waited for, and HBM sees full
+// lines instead of 16-byte pieces from different waves.
 //
 // Quantization.  The group absmax is a local max plus two cross-lane steps.
 // Rounding to the integer code uses the float32 adder: for |y| <= 7.0000005,
@@ -52,6 +57,7 @@ constexpr int kW = 8;                  // waves per workgroup
 constexpr int kThreads = kW * 64;
 constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
 constexpr size_t kLdsBudget = 152 * 1024;
+constexpr int kMaxRT2 = 5;             // two row tiles per block up to r = 80 (register budget)
 
 __device__ inline uint32_t cvt_bf16x2(float a, float b) {  // round-to-nearest-even pair
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
@@ -75,12 +81,20 @@ __device__ inline uint32_t pack8(const float* z) {  // 8 codes -> one dword
   return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
 }
 
-// groups in flight per wave: about 100 VGPRs of loaded data
+// groups in flight per wave
 template <int RT, int RTM>
 constexpr int window() {
-  constexpr int per_group = 8 * RTM + 8 * RT;
-  constexpr int w = 100 / per_group;
-  return w < 1 ? 1 : (w > 6 ? 6 : w);
+  return 1;
+}
+
+// LDS layout: inv_s [gslice * 64] floats | codes [16 RTM rows][gslice * 32 + 16 B]
+// | scales [16 RTM rows][gslice] floats; the T partials [waves][16 RTM][r]
+// reuse the same bytes at the end.  The 16-byte row pad spreads a wave's 16
+// rows over distinct banks.
+__host__ __device__ inline int code_pitch(int gslice) { return gslice * 32 + 16; }
+__host__ __device__ inline size_t lds_main_bytes(int rtm, int gslice) {
+  return (size_t)gslice * kGroup * 4 + (size_t)16 * rtm * code_pitch(gslice) +
+         (size_t)16 * rtm * gslice * 4;
 }
 
 // RT = r / 16 rank tiles; RTM row tiles per workgroup; gslice groups per K-slice.
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, float* __restrict__ sx,
     float* __restrict__ T, int gslice) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // inv_s [gslice*64] | T partials
+  extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int NL = RT > 0 ? 2 * RT : 1;
   constexpr int CH = window<RT, RTM>();
   const int tid = threadIdx.x;
@@ -104,7 +118,9 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   const int g_end = min(sg1, g_begin + per_wave);
   const int g_last = max(g_end - 1, sg0);         // a wave without groups re-reads a valid one
   float* inv_s = lds;                             // channels of the slice
-  float* tpart = lds + gslice * kGroup;
+  uint8_t* lcodes = reinterpret_cast<uint8_t*>(lds + gslice * kGroup);
+  float* lscales = reinterpret_cast<float*>(lcodes + 16 * RTM * code_pitch(gslice));
+  float* tpart = lds;                             // reused after the codes have left
 
   const int m0 = blockIdx.x * 16 * RTM;
   const int fr = lane & 15;
@@ -212,13 +228,10 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   auto store_group = [&](int g, const uint2* codes, const float* scales) {
 #pragma unroll
     for (int t = 0; t < RTM; ++t) {
-      const int row = m0 + 16 * t + fr;
-      if (row < M) {
-        uint8_t* qrow = qx + (size_t)row * (K / 2) + g * 32 + 4 * fk;
-        *reinterpret_cast<uint32_t*>(qrow) = codes[t].x;
-        *reinterpret_cast<uint32_t*>(qrow + 16) = codes[t].y;
-        if (fk == 0) sx[(size_t)row * G + g] = scales[t];
-      }
+      uint8_t* crow = lcodes + (16 * t + fr) * code_pitch(gslice) + (g - sg0) * 32 + 4 * fk;
+      *reinterpret_cast<uint32_t*>(crow) = codes[t].x;
+      *reinterpret_cast<uint32_t*>(crow + 16) = codes[t].y;
+      if (fk == 0) lscales[(16 * t + fr) * gslice + (g - sg0)] = scales[t];
     }
   };
   // Whole windows: process a slot, refill it with the group CH ahead, then
@@ -251,11 +264,29 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     }
   }
 
+  // codes and scales of the block's rows for the slice, as whole row segments
+  __syncthreads();
+  {
+    const int ng = sg1 - sg0;
+    const int chunks = 2 * ng;                      // 16-byte pieces per row
+    for (int e = tid; e < 16 * RTM * chunks; e += kThreads) {
+      const int rr = e / chunks, c = e - (e / chunks) * chunks;
+      if (m0 + rr < M)
+        *reinterpret_cast<uint4*>(qx + (size_t)(m0 + rr) * (K / 2) + sg0 * 32 + c * 16) =
+            *reinterpret_cast<const uint4*>(lcodes + rr * code_pitch(gslice) + c * 16);
+    }
+    for (int e = tid; e < 16 * RTM * ng; e += kThreads) {
+      const int rr = e / ng, c = e - (e / ng) * ng;
+      if (m0 + rr < M) sx[(size_t)(m0 + rr) * G + sg0 + c] = lscales[rr * gslice + c];
+    }
+  }
+
   if constexpr (RT > 0) {
     // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + i.
     // Partials [wave][row of the block][rank], summed over waves in order.
     constexpr int RB = 16 * RTM;
     float* Ts = T + (size_t)slice * M * r;
+    __syncthreads();                                // LDS is reused for the partials
 #pragma unroll
     for (int t = 0; t < RTM; ++t)
 #pragma unroll
@@ -275,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 }
 
 size_t lds_bytes(int rtm, int gslice, int r) {
-  return (size_t)gslice * kGroup * 4 + (size_t)kW * 16 * rtm * r * 4;
+  return std::max(lds_main_bytes(rtm, gslice), (size_t)kW * 16 * rtm * r * 4);
 }
 
 template <int RT, int RTM>
@@ -297,26 +328,30 @@ hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const
 template <int RT>
 hipError_t launch_rt(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
                      const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
-  if (p.rtm == 2) return launch<RT, 2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+  if constexpr (RT <= kMaxRT2)
+    if (p.rtm == 2) return launch<RT, 2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
   return launch<RT, 1>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
 }
 
 }  // namespace
 
 // Row tiles per workgroup and K-slices.  Two row tiles halve the L1 traffic
-// (worth it with a low-rank branch and enough rows); slices then restore
-// >= 256 workgroups, keeping >= 8 groups (one per wave) per slice, and are
-// added while the slice's LDS does not fit.
+// (worth it with a low-rank branch and enough rows).  Slices keep >= 256
+// workgroups and at most 48 groups per slice (a 12288-wide K measured 25 %
+// faster in 48-group slices than in 96-group ones: smaller blocks, two per
+// CU, and a shorter last wave), with >= 8 groups (one per wave) per slice,
+// and are added while the slice's LDS does not fit.
 K1Plan k1_plan(int M, int K, int r, bool one_slice) {
   K1Plan p;
   const int G = K / kGroup;
-  p.rtm = (r > 0 && M >= 2048) ? 2 : 1;
+  p.rtm = (r > 0 && r <= 16 * kMaxRT2 && M >= 2048) ? 2 : 1;
   int slices = 1;
   if (one_slice) {
     if (lds_bytes(p.rtm, G, r) > kLdsBudget) p.rtm = 1;
   } else {
     const int rb = (M + 16 * p.rtm - 1) / (16 * p.rtm);
-    slices = std::max(1, std::min((256 + rb - 1) / rb, G / kW));
+    slices = std::max((256 + rb - 1) / rb, (G + 47) / 48);
+    slices = std::max(1, std::min(slices, G / kW));
     while (slices < G && lds_bytes(p.rtm, (G + slices - 1) / slices, r) > kLdsBudget) ++slices;
   }
   p.gslice = (G + slices - 1) / slices;
