@@ -6,7 +6,7 @@ names and argument order (see include/svdq.h).  Host functions take numpy
 arrays; device functions take torch tensors that already live on the GPU
 (torch only supplies device memory and the current stream).
 
-The library must be built first (``python -m bit_diffusion_model_svdq_amd.build``);
+The library must be built first (``python bit_diffusion_model_svdq_amd/build.py``);
 importing this package without it raises an ImportError.
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with python -m bit_diffusion_model_svdq_amd.build")
+    raise ImportError(f"{LIB_PATH} is missing: build it with python bit_diffusion_model_svdq_amd/build.py")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTE
                 6: "SVDQ_ERR_HIP"}
 
 EXPORTS = [
-    "svdq_act_absmax_update", "svdq_pack_weights", "svdq_quantize_residual",
+    "svdq_act_absmax_update", "svdq_pack_weights", "svdq_quantize_residual", "svdq_append_lora",
     "svdq_forward_workspace_bytes", "svdq_linear_forward", "svdq_forward_quantize",
     "svdq_forward_gemm", "svdq_quantize_activations", "svdq_debug_group_partials",
     "svdq_status_string", "svdq_last_error",
@@ -55,6 +55,7 @@ _sig = {
     "svdq_act_absmax_update": [_P, ctypes.c_int64, _I, _P],
     "svdq_pack_weights": [_P, _I, _I, _P, ctypes.POINTER(svdq_pack_params), _P, _P, _P, _P, _P, _P],
     "svdq_quantize_residual": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
+    "svdq_append_lora": [_P, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_bytes": [_I, _I, _I, _I],
     "svdq_linear_forward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_forward_quantize": [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
@@ -135,6 +136,25 @@ def svdq_quantize_residual(W, smooth, L1, L2):
                                      _hp(L2) if r else None, r, _hp(Wq), _hp(ws))
     _check(st, "svdq_quantize_residual")
     return Wq, ws
+
+
+def svdq_append_lora(smooth, L1, L2, A, B):
+    """(L1' [r + rl, K], L2' [N, r + rl]): the packed layer's low-rank factors with a
+    LoRA (A [K, rl] down, B [rl, N] up, float32) appended; host arrays."""
+    A = _host(A, np.float32)
+    B = _host(B, np.float32)
+    K, rl = A.shape
+    N = B.shape[1]
+    s = _host(smooth, np.float32, (K,))
+    L1 = _host(L1, np.uint16)
+    L2 = _host(L2, np.uint16)
+    r = L1.shape[0] if (L1 is not None and L1.ndim == 2) else 0
+    L1o = np.empty((r + rl, K), np.uint16)
+    L2o = np.empty((N, r + rl), np.uint16)
+    st = _lib.svdq_append_lora(_hp(s), K, N, _hp(L1) if r else None, _hp(L2) if r else None, r,
+                               _hp(A), _hp(B), rl, _hp(L1o), _hp(L2o))
+    _check(st, "svdq_append_lora")
+    return L1o, L2o
 
 
 # ---------------------------------------------------------------- device side

@@ -1,6 +1,7 @@
 """Builds libsvdq.so in-tree: HIP sources with hipcc for gfx950, the host packer with g++.
 
-Run as ``python -m bit_diffusion_model_svdq_amd.build``.  Always recompiles.
+Run as ``python bit_diffusion_model_svdq_amd/build.py`` (by path: importing the package
+needs the library).  Always recompiles.
 """
 from __future__ import annotations
 

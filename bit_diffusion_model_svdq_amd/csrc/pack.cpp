@@ -533,4 +533,33 @@ svdq_status svdq_pack_weights(const float* W, int N, int K, const float* act_abs
   }
 }
 
+svdq_status svdq_append_lora(const float* smooth, int K, int N, const uint16_t* L1,
+                             const uint16_t* L2, int r, const float* A, const float* B, int rl,
+                             uint16_t* L1_out, uint16_t* L2_out) {
+  try {
+    if (!smooth || !A || !B || !L1_out || !L2_out) return fail(SVDQ_ERR_INVALID_ARG, "NULL buffer");
+    if (K < 1 || N < 1) return fail(SVDQ_ERR_INVALID_ARG, "bad shape K=%d N=%d", K, N);
+    if (r < 0 || rl < 1 || r + rl > 128)
+      return fail(SVDQ_ERR_INVALID_ARG, "ranks r=%d + rl=%d must stay within 1..128", r, rl);
+    if (r > 0 && (!L1 || !L2)) return fail(SVDQ_ERR_INVALID_ARG, "L1/L2 must not be NULL for r > 0");
+    const int r2 = r + rl;
+    // lora_down rows: the branch's r rows, then (diag(s) A)^T; A[k, j] * s[k] is
+    // exact in double, so one rounding to bf16
+    if (r > 0) memcpy(L1_out, L1, (size_t)r * K * sizeof(uint16_t));
+    for (int j = 0; j < rl; ++j)
+      for (int k = 0; k < K; ++k)
+        L1_out[(size_t)(r + j) * K + k] =
+            bf16_from_double((double)A[(size_t)k * rl + j] * (double)smooth[k]);
+    // lora_up rows: [L2 | B^T]
+    for (int n = 0; n < N; ++n) {
+      if (r > 0) memcpy(L2_out + (size_t)n * r2, L2 + (size_t)n * r, (size_t)r * sizeof(uint16_t));
+      for (int j = 0; j < rl; ++j)
+        L2_out[(size_t)n * r2 + r + j] = bf16_from_double((double)B[(size_t)j * N + n]);
+    }
+    return SVDQ_OK;
+  } catch (...) {
+    return fail(SVDQ_ERR_INVALID_ARG, "unexpected C++ exception");
+  }
+}
+
 }  // extern "C"

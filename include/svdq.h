@@ -103,6 +103,21 @@ svdq_status svdq_quantize_residual(const float* W, int N, int K, const float* sm
                                    const uint16_t* L1, const uint16_t* L2, int r, uint8_t* Wq,
                                    float* w_scales);
 
+/* Attach an off-the-shelf LoRA to a packed layer without re-quantizing it
+ * (abstract of "SVDQuant: Absorbing Outliers by Low-Rank Components for 4-Bit
+ * Diffusion Models": existing low-rank adapters are supported as they are).
+ * The adapter adds X A B to the output, A [K, rl] (down) and B [rl, N] (up),
+ * float32 row-major.  The low-rank branch sees X diag(s)^-1, so the adapter
+ * enters as extra rank:
+ *   L1_out [r + rl, K] = [L1 ; bf16((diag(s) A)^T)]  (A[k, j] s[k] rounded once)
+ *   L2_out [N, r + rl] = [L2 | bf16(B^T)]
+ * Wq and w_scales are unchanged.  The forward needs r + rl to be a multiple
+ * of 16 and at most 128.  L1/L2 may be NULL when r == 0.  Host memory,
+ * synchronous; outputs are untouched on an error. */
+svdq_status svdq_append_lora(const float* smooth, int K, int N, const uint16_t* L1,
+                             const uint16_t* L2, int r, const float* A, const float* B, int rl,
+                             uint16_t* L1_out, uint16_t* L2_out);
+
 /* ---------------------------------------------------------------- device */
 
 /* Workspace the forward needs, in bytes: the activation codes qx, their

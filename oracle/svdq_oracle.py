@@ -337,6 +337,26 @@ def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
     return Y
 
 
+def append_lora(s, L1_bf16, L2_bf16, A, B):
+    """Fold an off-the-shelf LoRA into the low-rank branch, leaving Q(R) as it is.
+
+    [Abs]: the engine takes existing low-rank adapters without re-quantizing the
+    4-bit weights.  A LoRA adds X A B to the output (A [K, rl] down, B [rl, N]
+    up).  The branch of E4 sees x_hat = X diag(s)^-1, and x_hat (diag(s) A) B =
+    X A B, so the adapter joins the branch as extra rank-rl factors:
+      L1' = [L1 ; bf16((diag(s) A)^T)]   [r + rl, K]   (A[k, j] * s[k], exact in float64)
+      L2' = [L2 | bf16(B^T)]             [N, r + rl]
+    """
+    s64 = np.asarray(s, dtype=F32).astype(F64)
+    A64 = np.asarray(A, dtype=F32).astype(F64)
+    B64 = np.asarray(B, dtype=F32).astype(F64)
+    L1n = bf16_from_f64((A64 * s64[:, None]).T)
+    L2n = bf16_from_f64(B64.T)
+    L1 = np.asarray(L1_bf16, dtype=np.uint16).reshape(-1, A64.shape[0])
+    L2 = np.asarray(L2_bf16, dtype=np.uint16).reshape(B64.shape[1], -1)
+    return np.concatenate([L1, L1n], axis=0), np.concatenate([L2, L2n], axis=1)
+
+
 def forward_exact(X_bf16, W, bias_bf16=None):
     """Unquantized reference X W^T + b in float64 (what E4 approximates)."""
     Y = bf16_to_f64(X_bf16) @ np.asarray(W, dtype=F32).astype(F64).T

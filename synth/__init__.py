@@ -31,6 +31,8 @@ _TID_U = 4
 _TID_V = 5
 _TID_BIAS = 6
 _TID_OUTLIER = 7
+_TID_LORA_A = 8
+_TID_LORA_B = 9
 
 
 @dataclasses.dataclass(frozen=True)
@@ -143,6 +145,14 @@ def weight(w: Workload) -> np.ndarray:
 def bias(w: Workload) -> np.ndarray:
     """bias as bf16 bits [N], N(0, bias_std)."""
     return f32_to_bf16_bits((_rng(w, _TID_BIAS).standard_normal(w.N) * w.bias_std).astype(np.float32))
+
+
+def lora_factors(w: Workload, rank: int = 16, std: float = 0.01):
+    """A seeded off-the-shelf LoRA for the layer: A [K, rank] (down) and
+    B [rank, N] (up), float32 N(0, std^2); it adds X A B to the output."""
+    A = (_rng(w, _TID_LORA_A).standard_normal((w.K, rank)) * std).astype(np.float32)
+    B = (_rng(w, _TID_LORA_B).standard_normal((rank, w.N)) * std).astype(np.float32)
+    return A, B
 
 
 def rng_for(name: str, tid: int) -> np.random.Generator:

@@ -203,3 +203,24 @@ def test_device_entry_points_validate_before_launching():
     assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 0, 300, 0, 16, a, None) == 1
     assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 10, 10, 0, 16, a, None) == 1
     assert L.svdq_debug_group_partials(a, mis, 256, 1024, 1024, 0, 16, 0, 16, a, None) == 3
+
+
+def test_append_lora_bit_exact_with_oracle():
+    """The library's LoRA concatenation gives the oracle's bytes (one rounding of
+    A[k, j] s[k] and of B[j, n] to bf16)."""
+    w = synth.WORKLOADS["tiny"]
+    g = np.random.default_rng(5)
+    K, N, r = w.K, w.N, 16
+    s = np.exp(g.uniform(-3, 3, K)).astype(np.float32)
+    L1 = synth.f32_to_bf16_bits(g.standard_normal((r, K)).astype(np.float32))
+    L2 = synth.f32_to_bf16_bits(g.standard_normal((N, r)).astype(np.float32))
+    A, B = synth.lora_factors(w)
+    L1n, L2n = S.svdq_append_lora(s, L1, L2, A, B)
+    L1o, L2o = O.append_lora(s, L1, L2, A, B)
+    np.testing.assert_array_equal(L1n, L1o)
+    np.testing.assert_array_equal(L2n, L2o)
+    L1z, L2z = S.svdq_append_lora(s, None, None, A, B)          # r = 0: the adapter alone
+    np.testing.assert_array_equal(L1z, L1o[r:])
+    np.testing.assert_array_equal(L2z, L2o[:, r:])
+    with pytest.raises(S.SvdqError):                           # r + rl > 128
+        S.svdq_append_lora(s, np.zeros((128, K), np.uint16), np.zeros((N, 128), np.uint16), A, B)

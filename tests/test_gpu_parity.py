@@ -232,6 +232,25 @@ def test_mlp_linears_full_launch_sampled_rows(name):
     np.testing.assert_array_equal(P, O.group_partials(qx_blk, p["Wq"][n0:n1]))
 
 
+def test_forward_with_appended_lora_r48():
+    """DiT projection with a rank-16 LoRA appended to the rank-32 branch (r = 48,
+    Wq untouched): the full launch against the oracle on sampled rows."""
+    say("forward dit_proj + LoRA r=48")
+    p = dict(packed("dit_proj"))
+    A, B = synth.lora_factors(synth.WORKLOADS["dit_proj"])
+    L1n, L2n = S.svdq_append_lora(p["s"], p["L1"], p["L2"], A, B)
+    L1o, L2o = O.append_lora(p["s"], p["L1"], p["L2"], A, B)
+    np.testing.assert_array_equal(L1n, L1o)
+    np.testing.assert_array_equal(L2n, L2o)
+    p.update(L1=L1o, L2=L2o, r=48)
+    d = to_device(p)
+    Yg = run_forward(p, d)
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(p["M"] - 16, p["M"]),
+                                     synth.rng_for("dit_proj", 33).choice(p["M"], 224, replace=False)]))
+    Yref = O.forward(p["X"][rows], p["s"], L1o, L2o, p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg[rows], Yref, "dit_proj + LoRA")
+
+
 def test_forward_remainder_split_ragged():
     """4300 x 256 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192, so 16 tiles
     (including the ragged last token tile) are cut along K into as many shares as

@@ -380,3 +380,49 @@ def test_quantizer_golden_examples():
         np.testing.assert_array_equal(q[0, :len(codes)], [int(c) for c in codes])
         n += 1
     assert n == 4
+
+
+# ------------------------------------------------------- LoRA concatenation
+def test_append_lora_adds_exactly_x_a_b():
+    """[Abs] LoRAs attach without re-quantization.  With power-of-two smoothing
+    factors and factors whose scaled values are bf16 numbers, every rounding on
+    the branch is exact, so the adapter's rows of T equal X A exactly and the
+    output grows by exactly (X A) B; Q(R) and the original rank are untouched."""
+    g = np.random.default_rng(11)
+    M, K, N, r, rl = 8, 128, 48, 16, 16
+    s = (2.0 ** g.integers(-3, 4, size=K)).astype(F32)
+    X = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(F32))
+    W = (g.standard_normal((N, K)) * 0.1).astype(F32)
+    A_scaled = O.bf16_to_f32(synth.f32_to_bf16_bits(g.standard_normal((K, rl)).astype(F32) * 0.05))
+    A = (A_scaled / s[:, None]).astype(F32)              # A * s is a bf16 number, exactly
+    B = O.bf16_to_f32(synth.f32_to_bf16_bits(g.standard_normal((rl, N)).astype(F32) * 0.05))
+    L1 = synth.f32_to_bf16_bits(g.standard_normal((r, K)).astype(F32) * 0.1)
+    L2 = synth.f32_to_bf16_bits(g.standard_normal((N, r)).astype(F32) * 0.1)
+    Wq, ws = O.quantize_residual(W, s, L1, L2)
+    L1n, L2n = O.append_lora(s, L1, L2, A, B)
+    assert L1n.shape == (r + rl, K) and L2n.shape == (N, r + rl)
+    np.testing.assert_array_equal(L1n[:r], L1)
+    np.testing.assert_array_equal(L2n[:, :r], L2)
+    _, _, T0, _ = O.quantize_activations(X, s, L1)
+    _, _, T1, _ = O.quantize_activations(X, s, L1n)
+    XA = O.bf16_to_f64(X) @ A.astype(F64)
+    np.testing.assert_array_equal(T1[:, :r], T0)
+    np.testing.assert_allclose(T1[:, r:], XA, rtol=1e-12, atol=1e-12 * np.abs(XA).max())
+    d = O.forward(X, s, L1n, L2n, Wq, ws) - O.forward(X, s, L1, L2, Wq, ws)
+    XAB = XA @ B.astype(F64)
+    assert np.max(np.abs(d - XAB)) <= 1e-12 * np.max(np.abs(XAB))
+
+
+def test_append_lora_transposes_and_scales_per_input_channel():
+    """The adapter's down factor is scaled per input channel k (not per output):
+    one nonzero A entry at (k, j) lands at L1'[r + j, k] as bf16(A[k, j] s[k])."""
+    K, N, rl = 64, 16, 16
+    s = np.ones(K, F32)
+    s[5] = 4.0
+    A = np.zeros((K, rl), F32)
+    A[5, 3] = 0.75
+    B = np.zeros((rl, N), F32)
+    B[3, 9] = -1.5
+    L1n, L2n = O.append_lora(s, np.zeros((0, K), np.uint16), np.zeros((N, 0), np.uint16), A, B)
+    assert O.bf16_to_f64(L1n)[3, 5] == 3.0 and np.count_nonzero(L1n) == 1
+    assert O.bf16_to_f64(L2n)[9, 3] == -1.5 and np.count_nonzero(L2n) == 1
