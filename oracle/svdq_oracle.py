@@ -366,6 +366,127 @@ def forward_exact(X_bf16, W, bias_bf16=None):
 
 
 # --------------------------------------------------------- comparisons
+# ------------------------------------------------------------- MXFP4 variant
+# The same three stages with Q(.) taken as the OCP microscaling format MXFP4:
+# blocks of 32 consecutive input channels share one power-of-two scale (an
+# E8M0 byte, 2^(byte - 127)) and each element is an FP4 E2M1 number.  The
+# pages give only "the quantization operation" for Q ([Term] 2.3, E4); this
+# variant is the MXFP4 reading of it, with the scale rule of the OCP MX v1.0
+# specification: shared exponent = floor(log2(amax)) - 2, where 2 is the
+# exponent of E2M1's largest value 6 = 1.5 * 2^2, and elements rounded to
+# nearest (ties to even) with saturation at +-6.
+MX_BLOCK = 32
+E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+E2M1_EMAX = 2
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 patterns: bit 3 is the sign, bits 0..2 index E2M1_MAG."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = np.asarray(E2M1_MAG, dtype=F64)[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_round(y) -> np.ndarray:
+    """Index (0..7) of the E2M1 magnitude nearest to y >= 0.
+
+    Ties go to the even index (IEEE ties-to-even on E2M1's one significand
+    bit); values beyond 6 land on 6 (saturation).
+    """
+    y = np.asarray(y, dtype=F64)
+    mags = np.asarray(E2M1_MAG, dtype=F64)
+    best = np.zeros(y.shape, dtype=np.int64)
+    best_d = np.abs(y - mags[0])
+    for i in range(1, 8):
+        d = np.abs(y - mags[i])
+        better = (d < best_d) | ((d == best_d) & (i % 2 == 0))
+        best = np.where(better, i, best)
+        best_d = np.where(better, d, best_d)
+    return best
+
+
+def mx_shared_exponent(amax) -> np.ndarray:
+    """floor(log2(amax)) - E2M1_EMAX, clipped to the E8M0 range [-127, 127];
+    an all-zero block gets -127."""
+    amax = np.asarray(amax, dtype=F64)
+    m, x = np.frexp(amax)                 # amax = m * 2^x, 0.5 <= m < 1, so floor(log2) = x - 1
+    e = np.clip(x.astype(np.int64) - 1 - E2M1_EMAX, -127, 127)
+    return np.where(amax > 0, e, -127)
+
+
+def quantize_mx(v32):
+    """MXFP4 of float32 rows [R, K] (K % 32 == 0).
+
+    Returns (codes uint8 [R, K] of 4-bit patterns, exponents int64 [R, K/32]).
+    The sign bit is the sign of the input (so a negative value that rounds to
+    zero keeps it); scaling by 2^-e is exact.
+    """
+    v = np.asarray(v32, dtype=F32).astype(F64)
+    R, K = v.shape
+    blocks = v.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    e = mx_shared_exponent(np.max(np.abs(blocks), axis=2))
+    y = np.abs(blocks) / np.exp2(e.astype(F64))[:, :, None]
+    idx = e2m1_round(y)
+    sign = np.signbit(blocks).astype(np.int64)
+    codes = (idx | (sign << 3)).astype(np.uint8)
+    return codes.reshape(R, K), e
+
+
+def e8m0_bytes(e) -> np.ndarray:
+    return (np.asarray(e, dtype=np.int64) + 127).astype(np.uint8)
+
+
+def unpack_codes4(b) -> np.ndarray:
+    """Raw 4-bit patterns [R, 2 * C] of packed bytes [R, C] (even index in the low nibble)."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty((b.shape[0], b.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def quantize_residual_mx(W, s, L1, L2):
+    """Stage three with MXFP4: (Wq packed [N, K/2], w_e8m0 [N, K/32]) of R = W diag(s) - L2 L1."""
+    R = residual(smooth_weight(W, s), L1, L2)
+    codes, e = quantize_mx(R)
+    return pack_nibbles(codes.astype(np.int64)), e8m0_bytes(e)
+
+
+def quantize_activations_mx(X_bf16, s, L1_bf16=None):
+    """(qx packed [M, K/2], sx_e8m0 [M, K/32], T [M, r], x_hat) with MXFP4 codes of x_hat."""
+    xh = smooth_activations(X_bf16, s)
+    codes, e = quantize_mx(xh)
+    if L1_bf16 is not None and np.asarray(L1_bf16).size:
+        T = xh.astype(F64) @ bf16_to_f64(L1_bf16).T
+    else:
+        T = np.zeros((xh.shape[0], 0), dtype=F64)
+    return pack_nibbles(codes.astype(np.int64)), e8m0_bytes(e), T, xh
+
+
+def forward_mx(X_bf16, s, L1_bf16, L2_bf16, Wq, w_e8m0, bias_bf16=None):
+    """Y = Q_mx(X diag(s)^-1) Q_mx(R) + (X diag(s)^-1 L1^T) L2^T + b in float64.
+
+    The low-bit term is sum over blocks b of 2^(ea[m,b] + eb[n,b]) times the
+    exact dot product of the two blocks' E2M1 values.
+    """
+    qx, sxe, T, _ = quantize_activations_mx(X_bf16, s, L1_bf16)
+    a = e2m1_value(unpack_codes4(qx))
+    w = e2m1_value(unpack_codes4(Wq))
+    ea = sxe.astype(np.int64) - 127
+    eb = np.asarray(w_e8m0).astype(np.int64) - 127
+    M, K = a.shape
+    N = w.shape[0]
+    main = np.zeros((M, N), dtype=F64)
+    for b in range(K // MX_BLOCK):
+        sl = slice(b * MX_BLOCK, (b + 1) * MX_BLOCK)
+        main += np.exp2((ea[:, b][:, None] + eb[:, b][None, :]).astype(F64)) * (a[:, sl] @ w[:, sl].T)
+    low = T @ bf16_to_f64(L2_bf16).T if T.shape[1] > 0 else np.zeros((M, N), dtype=F64)
+    Y = main + low
+    if bias_bf16 is not None:
+        Y = Y + bf16_to_f64(bias_bf16)[None, :]
+    return Y
+
+
 def rel_fro(Y, Yref) -> float:
     Y = np.asarray(Y, dtype=F64)
     Yref = np.asarray(Yref, dtype=F64)

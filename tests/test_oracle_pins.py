@@ -426,3 +426,127 @@ def test_append_lora_transposes_and_scales_per_input_channel():
     L1n, L2n = O.append_lora(s, np.zeros((0, K), np.uint16), np.zeros((N, 0), np.uint16), A, B)
     assert O.bf16_to_f64(L1n)[3, 5] == 3.0 and np.count_nonzero(L1n) == 1
     assert O.bf16_to_f64(L2n)[9, 3] == -1.5 and np.count_nonzero(L2n) == 1
+
+
+# ------------------------------------------------------------------- MXFP4
+def test_e2m1_decode_table():
+    """All 16 E2M1 patterns: sign bit 3, then (exponent, significand) = bits 2..1, bit 0."""
+    want = [0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
+    got = O.e2m1_value(np.arange(16))
+    np.testing.assert_array_equal(got, want)
+    assert np.signbit(got[8])
+
+
+def test_e2m1_round_ties_even_and_saturation():
+    """Hand-derived: midpoints go to the even significand (0, 1, 1, 2, 2, 4, 4); past 5
+    everything is 6, including values far beyond the largest E2M1 number."""
+    y = [0.0, 0.2499, 0.25, 0.2501, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0,
+         5.0001, 6.0, 7.0, 100.0]
+    want_val = [0, 0, 0, 0.5, 0.5, 1, 1, 1, 1.5, 2, 2, 2, 3, 4, 4, 4, 6, 6, 6, 6]
+    idx = O.e2m1_round(y)
+    np.testing.assert_array_equal(np.asarray(O.E2M1_MAG)[idx], want_val)
+
+
+def test_mx_shared_exponent_rule():
+    """OCP MX v1.0 with E2M1 (largest value 1.5 * 2^2): e = floor(log2 amax) - 2."""
+    amax = [1.0, 1.5, 3.999, 4.0, 6.0, 7.99, 8.0, 0.75, 2.0 ** -100, 0.0, 1e-45, 3e38]
+    want = [-2, -2, -1, 0, 0, 0, 1, -3, -102, -127, -127, 125]
+    np.testing.assert_array_equal(O.mx_shared_exponent(np.asarray(amax, F32)), want)
+
+
+def test_mx_block_error_bound_and_range():
+    """Every element lies within half a grid step of its code (the step is 0.5, 1 or 2
+    times 2^e in [0, 2), [2, 4), [4, 6]), except saturated ones, which the scale rule
+    keeps below 8 * 2^e, i.e. within 2 * 2^e of 6 * 2^e; codes are valid patterns."""
+    g = np.random.default_rng(21)
+    v = (g.standard_normal((64, 256)) * np.exp(g.uniform(-8, 8, (64, 1)))).astype(F32)
+    v[:, :40] *= 30.0
+    codes, e = O.quantize_mx(v)
+    assert codes.max() <= 15
+    scale = np.repeat(np.exp2(e.astype(F64)), 32, axis=1)
+    q = O.e2m1_value(codes) * scale
+    y = np.abs(v.astype(F64)) / scale
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    err = np.abs(v.astype(F64) - q)
+    sat = y > 6
+    assert np.all(err[~sat] <= 0.5 * step[~sat] * scale[~sat])
+    assert np.all(y < 8) and np.all(err[sat] <= 2 * scale[sat])
+
+
+def test_mx_power_of_two_equivariance():
+    g = np.random.default_rng(22)
+    v = g.standard_normal((8, 128)).astype(F32)
+    c0, e0 = O.quantize_mx(v)
+    c1, e1 = O.quantize_mx(v * F32(2.0 ** 7))
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(e1, e0 + 7)
+
+
+def _mx_exact_rows(g, rows, K):
+    """Rows that MXFP4 represents exactly: E2M1 values times a power of two per block,
+    with one +-4 or +-6 per block so that the scale rule picks that power."""
+    codes = g.integers(0, 16, size=(rows, K))
+    codes[:, ::32] = g.choice([6, 7, 14, 15], size=(rows, K // 32))
+    e = g.integers(-4, 5, size=(rows, K // 32))
+    return O.e2m1_value(codes) * np.repeat(np.exp2(e.astype(F64)), 32, axis=1)
+
+
+def test_mx_forward_lossless_limit():
+    """With X and W exactly representable in MXFP4, s = 1 and no low-rank branch, the
+    MXFP4 forward is exactly X W^T + b: this pins the block pairing along K, the
+    addition of the two block exponents and the packing order of the codes."""
+    g = np.random.default_rng(23)
+    M, N, K = 6, 5, 128
+    X = synth.f32_to_bf16_bits(_mx_exact_rows(g, M, K).astype(F32))
+    W = _mx_exact_rows(g, N, K).astype(F32)
+    assert np.array_equal(O.bf16_to_f64(X), _mx_exact_rows(np.random.default_rng(23), M, K))
+    s = np.ones(K, F32)
+    b = synth.f32_to_bf16_bits(g.standard_normal(N).astype(F32))
+    none1, none2 = np.zeros((0, K), np.uint16), np.zeros((N, 0), np.uint16)
+    Wq, we = O.quantize_residual_mx(W, s, none1, none2)
+    Y = O.forward_mx(X, s, none1, none2, Wq, we, b)
+    np.testing.assert_array_equal(Y, O.forward_exact(X, W, b))
+
+
+def test_mx_forward_matches_exact_rationals():
+    """Brute force with Fractions on a tiny layer: the MXFP4 contract evaluated exactly
+    (block exponents from each block's absmax, nearest E2M1 values, exact sums) equals
+    the oracle's float64 forward (r = 0, s = 1, dyadic inputs: every sum is exact)."""
+    from fractions import Fraction as Fr
+    g = np.random.default_rng(24)
+    M, N, K = 2, 3, 64
+    X = synth.f32_to_bf16_bits((g.integers(-64, 64, (M, K)) / 16.0).astype(F32))
+    W = (g.integers(-64, 64, (N, K)) / 32.0).astype(F32)
+    s = np.ones(K, F32)
+    none1, none2 = np.zeros((0, K), np.uint16), np.zeros((N, 0), np.uint16)
+    Wq, we = O.quantize_residual_mx(W, s, none1, none2)
+    Y = O.forward_mx(X, s, none1, none2, Wq, we)
+    mags = [Fr(0), Fr(1, 2), Fr(1), Fr(3, 2), Fr(2), Fr(3), Fr(4), Fr(6)]
+
+    def q_block(vals):
+        vals = [Fr(float(v)) for v in vals]
+        amax = max(abs(v) for v in vals)
+        e = -127
+        if amax:
+            fl = 0
+            while Fr(2) ** (fl + 1) <= amax:
+                fl += 1
+            while Fr(2) ** fl > amax:
+                fl -= 1
+            e = fl - 2
+        out = []
+        for v in vals:
+            y = abs(v) / Fr(2) ** e
+            d = [abs(y - m) for m in mags]
+            best = min(range(8), key=lambda i: (d[i], i % 2))
+            out.append((-1 if v < 0 else 1) * mags[best] * Fr(2) ** e)
+        return out
+
+    xv = O.bf16_to_f64(X)
+    for m in range(M):
+        for n in range(N):
+            acc = Fr(0)
+            for blk in range(K // 32):
+                sl = slice(32 * blk, 32 * blk + 32)
+                acc += sum(a * w for a, w in zip(q_block(xv[m, sl]), q_block(W[n, sl])))
+            assert Fr(Y[m, n]) == acc
