@@ -34,6 +34,8 @@ EXPORTS = [
     "svdq_forward_workspace_bytes", "svdq_linear_forward", "svdq_forward_quantize",
     "svdq_forward_gemm", "svdq_quantize_activations", "svdq_debug_group_partials",
     "svdq_status_string", "svdq_last_error",
+    "svdq_quantize_residual_mxfp4", "svdq_forward_workspace_bytes_mxfp4", "svdq_linear_forward_mxfp4",
+    "svdq_forward_quantize_mxfp4", "svdq_forward_gemm_mxfp4", "svdq_quantize_activations_mxfp4",
 ]
 
 
@@ -62,6 +64,12 @@ _sig = {
     "svdq_forward_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_quantize_activations": [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P],
     "svdq_debug_group_partials": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "svdq_quantize_residual_mxfp4": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
+    "svdq_forward_workspace_bytes_mxfp4": [_I, _I, _I, _I],
+    "svdq_linear_forward_mxfp4": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_quantize_mxfp4": [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_gemm_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "svdq_quantize_activations_mxfp4": [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P],
     "svdq_status_string": [_I],
     "svdq_last_error": [],
 }
@@ -70,6 +78,7 @@ for _name, _args in _sig.items():
     _f.argtypes = _args
     _f.restype = _I
 _lib.svdq_forward_workspace_bytes.restype = ctypes.c_size_t
+_lib.svdq_forward_workspace_bytes_mxfp4.restype = ctypes.c_size_t
 _lib.svdq_status_string.restype = ctypes.c_char_p
 _lib.svdq_last_error.restype = ctypes.c_char_p
 
@@ -223,3 +232,59 @@ def svdq_status_string(status: int) -> str:
 
 def svdq_last_error() -> str:
     return _lib.svdq_last_error().decode()
+
+
+# ------------------------------------------------------------ MXFP4 variant
+def svdq_quantize_residual_mxfp4(W, smooth, L1, L2):
+    """Wq [N, K/2] (E2M1 codes) and w_e8m0 [N, K/32] from W, s, L1 [r, K], L2 [N, r] (host arrays)."""
+    W = _host(W, np.float32)
+    N, K = W.shape
+    s = _host(smooth, np.float32, (K,))
+    L1 = _host(L1, np.uint16)
+    L2 = _host(L2, np.uint16)
+    r = L1.shape[0] if (L1 is not None and L1.ndim == 2) else 0
+    Wq = np.empty((N, K // 2), np.uint8)
+    we = np.empty((N, K // 32), np.uint8)
+    st = _lib.svdq_quantize_residual_mxfp4(_hp(W), N, K, _hp(s), _hp(L1) if r else None,
+                                           _hp(L2) if r else None, r, _hp(Wq), _hp(we))
+    _check(st, "svdq_quantize_residual_mxfp4")
+    return Wq, we
+
+
+def svdq_forward_workspace_bytes_mxfp4(M: int, K: int, N: int, r: int) -> int:
+    return int(_lib.svdq_forward_workspace_bytes_mxfp4(M, K, N, r))
+
+
+def svdq_linear_forward_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, Y, workspace, stream=None):
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_linear_forward_mxfp4(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                        _dp(w_e8m0), _dp(bias), _dp(Y), _dp(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_linear_forward_mxfp4")
+    return Y
+
+
+def svdq_forward_quantize_mxfp4(X, smooth, L1, workspace, stream=None):
+    M, K = X.shape
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_forward_quantize_mxfp4(_dp(X), M, K, r, _dp(smooth), _dp(L1), _dp(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_forward_quantize_mxfp4")
+
+
+def svdq_forward_gemm_mxfp4(M, K, L2, Wq, w_e8m0, bias, Y, workspace, r, stream=None):
+    N = Wq.shape[0]
+    st = _lib.svdq_forward_gemm_mxfp4(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_e8m0), _dp(bias), _dp(Y),
+                                      _dp(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check(st, "svdq_forward_gemm_mxfp4")
+
+
+def svdq_quantize_activations_mxfp4(X, smooth, L1, qx, sx_e8m0, T, stream=None):
+    M, K = X.shape
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_quantize_activations_mxfp4(_dp(X), M, K, _dp(smooth), _dp(L1), r, _dp(qx),
+                                              _dp(sx_e8m0), _dp(T), _stream(stream))
+    _check(st, "svdq_quantize_activations_mxfp4")

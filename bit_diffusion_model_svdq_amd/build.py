@@ -30,7 +30,7 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fopenmp",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
-HIP_SOURCES = ["svdq_api.hip", "k1_smooth_quant.hip", "k2_w4a4_gemm.hip"]
+HIP_SOURCES = ["svdq_api.hip", "k1_smooth_quant.hip", "k2_w4a4_gemm.hip", "k2_mxfp4_gemm.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 

@@ -37,6 +37,16 @@
 // bit pattern is the packed code.  |y| cannot exceed 7 * (1 + 2^-24) because
 // inv = fl32(7 / amax), so no clamp is needed.
 //
+// MXFP4 (template flag MX).  The same kernel quantizes each block of 32
+// channels (a lane's 8 + the 3 other lanes of its row) to FP4 E2M1 with one
+// E8M0 scale: the shared exponent floor(log2 amax) - 2 is the block absmax's
+// exponent field minus 129 (clamped at -127), i.e. the E8M0 byte is
+// max(exponent field - 2, 0), and v_cvt_scalef32_pk_fp4_f32 divides by the
+// power-of-two scale and rounds to nearest even with saturation, two
+// elements per instruction, keeping the sign of a value that rounds to zero.
+// A block whose scale would be the subnormal 2^-127 (absmax < 2^-125) is
+// converted as v * 2^127 with scale 1 instead.
+//
 // lora_down.  x_hat enters the MFMA as a bf16 hi/lo pair (hi = x_hat with the
 // low 16 bits cleared, lo = bf16(x_hat - hi), an exact difference), so T keeps
 // ~16 significant bits.  The waves' partial T are summed in LDS in a fixed
@@ -98,10 +108,10 @@ __host__ __device__ inline size_t lds_main_bytes(int rtm, int gslice) {
 }
 
 // RT = r / 16 rank tiles; RTM row tiles per workgroup; gslice groups per K-slice.
-template <int RT, int RTM>
+template <int RT, int RTM, bool MX>
 __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
-    const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, float* __restrict__ sx,
+    const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, void* __restrict__ sx_out,
     float* __restrict__ T, int gslice) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int NL = RT > 0 ? 2 * RT : 1;
@@ -119,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   const int g_last = max(g_end - 1, sg0);         // a wave without groups re-reads a valid one
   float* inv_s = lds;                             // channels of the slice
   uint8_t* lcodes = reinterpret_cast<uint8_t*>(lds + gslice * kGroup);
-  float* lscales = reinterpret_cast<float*>(lcodes + 16 * RTM * code_pitch(gslice));
+  // per row and group: the float32 scale's bits (int4) or the two E8M0 bytes (MX)
+  uint32_t* lscales = reinterpret_cast<uint32_t*>(lcodes + 16 * RTM * code_pitch(gslice));
   float* tpart = lds;                             // reused after the codes have left
 
   const int m0 = blockIdx.x * 16 * RTM;
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 
   // One group of one row tile from registers: codes, scale, and the lora_down MFMAs.
   auto process = [&](int g, uint4 va, uint4 vb, const uint4* lf, f32x4* at, uint2& codes,
-                     float& scale) {
+                     uint32_t& scale) {
     const int k0 = (g - sg0) * kGroup + 8 * fk;
     const uint32_t w[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
     float xh[16];
@@ -189,18 +200,52 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
         xh[8 * c + 2 * i + 1] = __uint_as_float(w[4 * c + i] & 0xFFFF0000u) * is[2 * i + 1];
       }
     }
-    float amax = 0.f;
+    if constexpr (MX) {
+      // blocks: channels 0..31 (xh[0..7] of the row's four lanes), 32..63 (xh[8..15])
+      float am[2] = {0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    scale = amax / 7.0f;
-    const float inv = amax > 0.f ? 7.0f / amax : 0.f;
-    float z[16];
+      for (int i = 0; i < 16; ++i) am[i >> 3] = fmaxf(am[i >> 3], fabsf(xh[i]));
+      uint32_t bytes[2], words[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
-    codes.x = pack8(z);
-    codes.y = pack8(z + 8);
+      for (int b = 0; b < 2; ++b) {
+        am[b] = fmaxf(am[b], __shfl_xor(am[b], 16));
+        am[b] = fmaxf(am[b], __shfl_xor(am[b], 32));
+        const int ef = (int)((__float_as_uint(am[b]) >> 23) & 0xFFu);
+        bytes[b] = (uint32_t)max(ef - 2, 0);
+        const float* v = xh + 8 * b;
+        float sc = __uint_as_float(bytes[b] << 23);            // 2^(byte - 127)
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = v[i];
+        if (bytes[b] == 0u) {                                   // 2^-127 is not a normal float
+          sc = 1.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = v[i] * 0x1p127f;   // exact: |v| < 2^-125
+        }
+        uint32_t w = 0u;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], sc, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], sc, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], sc, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], sc, 3);
+        words[b] = w;
+      }
+      codes.x = words[0];
+      codes.y = words[1];
+      scale = bytes[0] | (bytes[1] << 8);
+    } else {
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      scale = __float_as_uint(amax / 7.0f);
+      const float inv = amax > 0.f ? 7.0f / amax : 0.f;
+      float z[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
+      codes.x = pack8(z);
+      codes.y = pack8(z + 8);
+    }
     if constexpr (RT > 0) {
       uint32_t hi[8], lo[8];
 #pragma unroll
@@ -225,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     }
   };
 
-  auto store_group = [&](int g, const uint2* codes, const float* scales) {
+  auto store_group = [&](int g, const uint2* codes, const uint32_t* scales) {
 #pragma unroll
     for (int t = 0; t < RTM; ++t) {
       uint8_t* crow = lcodes + (16 * t + fr) * code_pitch(gslice) + (g - sg0) * 32 + 4 * fk;
@@ -243,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       uint2 codes[RTM];
-      float scales[RTM];
+      uint32_t scales[RTM];
 #pragma unroll
       for (int t = 0; t < RTM; ++t)
         process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
@@ -256,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   for (int j = 0; j < CH; ++j) {
     if (gb + j < g_end) {
       uint2 codes[RTM];
-      float scales[RTM];
+      uint32_t scales[RTM];
 #pragma unroll
       for (int t = 0; t < RTM; ++t)
         process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
@@ -277,7 +322,16 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     }
     for (int e = tid; e < 16 * RTM * ng; e += kThreads) {
       const int rr = e / ng, c = e - (e / ng) * ng;
-      if (m0 + rr < M) sx[(size_t)(m0 + rr) * G + sg0 + c] = lscales[rr * gslice + c];
+      if (m0 + rr < M) {
+        const uint32_t v = lscales[rr * gslice + c];
+        if constexpr (MX) {
+          uint8_t* d = static_cast<uint8_t*>(sx_out) + (size_t)(m0 + rr) * 2 * G + 2 * (sg0 + c);
+          d[0] = (uint8_t)(v & 0xFFu);
+          d[1] = (uint8_t)(v >> 8);
+        } else {
+          static_cast<float*>(sx_out)[(size_t)(m0 + rr) * G + sg0 + c] = __uint_as_float(v);
+        }
+      }
     }
   }
 
@@ -309,11 +363,11 @@ size_t lds_bytes(int rtm, int gslice, int r) {
   return std::max(lds_main_bytes(rtm, gslice), (size_t)kW * 16 * rtm * r * 4);
 }
 
-template <int RT, int RTM>
+template <int RT, int RTM, bool MX>
 hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
-                  const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
+                  const uint16_t* L1, uint8_t* qx, void* sx, float* T, hipStream_t stream) {
   const size_t lds = lds_bytes(RTM, p.gslice, r);
-  auto kern = smooth_quant_lora_down_kernel<RT, RTM>;
+  auto kern = smooth_quant_lora_down_kernel<RT, RTM, MX>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -325,12 +379,31 @@ hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const
   return hipGetLastError();
 }
 
-template <int RT>
+template <int RT, bool MX>
 hipError_t launch_rt(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
-                     const uint16_t* L1, uint8_t* qx, float* sx, float* T, hipStream_t stream) {
+                     const uint16_t* L1, uint8_t* qx, void* sx, float* T, hipStream_t stream) {
   if constexpr (RT <= kMaxRT2)
-    if (p.rtm == 2) return launch<RT, 2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-  return launch<RT, 1>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    if (p.rtm == 2) return launch<RT, 2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+  return launch<RT, 1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+}
+
+template <bool MX>
+hipError_t dispatch(const uint16_t* X, int M, int K, int r, const float* smooth,
+                    const uint16_t* L1, uint8_t* qx, void* sx, float* T, bool one_slice,
+                    hipStream_t stream) {
+  const K1Plan p = k1_plan(M, K, r, one_slice);
+  switch (r / 16) {
+    case 0: return launch_rt<0, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 1: return launch_rt<1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 2: return launch_rt<2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 3: return launch_rt<3, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 4: return launch_rt<4, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 5: return launch_rt<5, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 6: return launch_rt<6, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 7: return launch_rt<7, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 8: return launch_rt<8, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -362,19 +435,14 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice) {
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
                                          float* sx, float* T, bool one_slice, hipStream_t stream) {
-  const K1Plan p = k1_plan(M, K, r, one_slice);
-  switch (r / 16) {
-    case 0: return launch_rt<0>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 1: return launch_rt<1>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 2: return launch_rt<2>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 3: return launch_rt<3>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 4: return launch_rt<4>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 5: return launch_rt<5>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 6: return launch_rt<6>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 7: return launch_rt<7>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 8: return launch_rt<8>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch<false>(X, M, K, r, smooth, L1, qx, sx, T, one_slice, stream);
+}
+
+hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int r,
+                                            const float* smooth, const uint16_t* L1, uint8_t* qx,
+                                            uint8_t* sx_e8m0, float* T, bool one_slice,
+                                            hipStream_t stream) {
+  return dispatch<true>(X, M, K, r, smooth, L1, qx, sx_e8m0, T, one_slice, stream);
 }
 
 }  // namespace svdq

@@ -37,6 +37,7 @@
 // of qx and Wq in its own L2.
 #include <algorithm>
 
+#include "gemm_tail.h"
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -393,81 +394,8 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
 
-  for (int j0 = 0; j0 < r; j0 += 32) {
-    const int j = j0 + 8 * fk;
-    const bool j_ok = j < r;
-    bf16x8 thi[C::TM], tlo[C::TM];
-#pragma unroll
-    for (int t = 0; t < C::TM; ++t) {
-      const int m = m0 + wr + 16 * t + fr;
-      float tv[8];
-      if (j_ok && m < row1) {
-        // T arrives as t_slices partial sums (one per K-slice of the quantize
-        // kernel), added here in slice order
-        const float* tp = T + (size_t)m * r + j;
-        float4 a = *reinterpret_cast<const float4*>(tp);
-        float4 b = *reinterpret_cast<const float4*>(tp + 4);
-        for (int sl = 1; sl < t_slices; ++sl) {
-          const float4 a2 = *reinterpret_cast<const float4*>(tp + sl * t_stride);
-          const float4 b2 = *reinterpret_cast<const float4*>(tp + sl * t_stride + 4);
-          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-          b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
-        }
-        tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
-        tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tv[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)tv[e];
-        thi[t][e] = h;
-        tlo[t][e] = (__bf16)(tv[e] - (float)h);
-      }
-    }
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      const int n = n0 + wc + 16 * tn + fr;
-      const bf16x8 lf = (j_ok && n < col1)
-                            ? as_bf16x8(*reinterpret_cast<const uint4*>(L2 + (size_t)n * r + j))
-                            : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-#pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm) {
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[tm], lf, acc[tm][tn], 0, 0, 0);
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[tm], lf, acc[tm][tn], 0, 0, 0);
-      }
-    }
-  }
-
-  // bias, bf16, then the tile goes through LDS (columns swizzled by 16 elements
-  // per group of 4 rows, so that the 4 row groups of a write hit distinct banks)
-  // and leaves as 16-byte row segments.
-  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) {
-    const int col = wc + 16 * tn + fr;
-    const int n = n0 + col;
-    const float bv = (bias && n < col1) ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wr + 16 * tm + 4 * fk + i;
-        otile[row * C::BN + (col ^ (16 * ((row >> 2) & 3)))] =
-            __builtin_bit_cast(uint16_t, (__bf16)(acc[tm][tn][i] + bv));
-      }
-  }
-  __syncthreads();
-  constexpr int CPR = C::BN / 8;   // 16-byte chunks per output row
-  for (int c = tid; c < C::BM * CPR; c += C::THREADS) {
-    const int row = c / CPR, ch = c - (c / CPR) * CPR;
-    const int m = m0 + row, n = n0 + 8 * ch;
-    if (m < row1 && n < col1) {
-      const uint4 v = *reinterpret_cast<const uint4*>(otile + row * C::BN + 8 * (ch ^ (2 * ((row >> 2) & 3))));
-      *reinterpret_cast<uint4*>(Y + (size_t)m * ldy + n) = v;
-    }
-  }
+  tail::lowrank_bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
+      acc, T, t_slices, t_stride, r, L2, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid, lds);
 }
 
 int cu_count() {

@@ -17,6 +17,7 @@
 // relative accuracy only for singular values far below sigma_1, which the
 // rank-r branch does not keep.
 #include <math.h>
+#include <cmath>
 #include <stdint.h>
 #include <string.h>
 
@@ -361,9 +362,45 @@ void quantize_group(const float* v, uint8_t* packed, float* scale_out) {
   *scale_out = scale;
 }
 
-void residual_quantize(const float* W, int N, int K, const float* s, const uint16_t* L1,
-                       const uint16_t* L2, int r, uint8_t* Wq, float* w_scales) {
-  const int G = K / kGroup;
+// MXFP4 block of 32 (OCP MX v1.0): E8M0 scale 2^e with e = floor(log2 amax) - 2
+// (2 = exponent of E2M1's largest value 6), clamped to [-127, 127], -127 for an
+// all-zero block; each element is the nearest E2M1 value of v / 2^e, ties to
+// the even significand, saturating at 6, with the sign of v.
+constexpr double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int e2m1_code(float v, int e) {
+  const double y = std::ldexp(std::fabs((double)v), -e);   // exact: a power-of-two scaling
+  int best = 0;
+  double bd = y;
+  for (int i = 1; i < 8; ++i) {
+    const double d = std::fabs(y - kE2M1[i]);
+    if (d < bd || (d == bd && (i & 1) == 0)) {
+      best = i;
+      bd = d;
+    }
+  }
+  return best | (std::signbit(v) ? 8 : 0);
+}
+
+void quantize_block_mx(const float* v, uint8_t* packed, uint8_t* e8m0) {
+  float a = 0.f;
+  for (int i = 0; i < 32; ++i) a = std::max(a, fabsf(v[i]));
+  int e = -127;
+  if (a > 0.f) {
+    int x = 0;
+    std::frexp((double)a, &x);                 // a = m 2^x, m in [0.5, 1): floor(log2 a) = x - 1
+    e = std::min(std::max(x - 1 - 2, -127), 127);
+  }
+  for (int i = 0; i < 32; i += 2)
+    packed[i / 2] = (uint8_t)(e2m1_code(v[i], e) | (e2m1_code(v[i + 1], e) << 4));
+  *e8m0 = (uint8_t)(e + 127);
+}
+
+// R = fl32(W diag(s) - L2 L1) row by row (sum over j ascending in double, from
+// the stored bf16 factors), then quantize(R row, n).
+template <class Q>
+void residual_rows(const float* W, int N, int K, const float* s, const uint16_t* L1,
+                   const uint16_t* L2, int r, Q quantize) {
 #pragma omp parallel
   {
     std::vector<double> l2row(r);
@@ -377,11 +414,29 @@ void residual_quantize(const float* W, int N, int K, const float* s, const uint1
         const double what = (double)W[(size_t)n * K + k] * (double)s[k];
         R[k] = (float)(what - acc);
       }
-      for (int g = 0; g < G; ++g)
-        quantize_group(&R[(size_t)g * kGroup], Wq + (size_t)n * (K / 2) + g * (kGroup / 2),
-                       &w_scales[(size_t)n * G + g]);
+      quantize(R.data(), n);
     }
   }
+}
+
+void residual_quantize(const float* W, int N, int K, const float* s, const uint16_t* L1,
+                       const uint16_t* L2, int r, uint8_t* Wq, float* w_scales) {
+  const int G = K / kGroup;
+  residual_rows(W, N, K, s, L1, L2, r, [&](const float* R, int n) {
+    for (int g = 0; g < G; ++g)
+      quantize_group(&R[(size_t)g * kGroup], Wq + (size_t)n * (K / 2) + g * (kGroup / 2),
+                     &w_scales[(size_t)n * G + g]);
+  });
+}
+
+void residual_quantize_mx(const float* W, int N, int K, const float* s, const uint16_t* L1,
+                          const uint16_t* L2, int r, uint8_t* Wq, uint8_t* w_e8m0) {
+  const int B = K / 32;
+  residual_rows(W, N, K, s, L1, L2, r, [&](const float* R, int n) {
+    for (int b = 0; b < B; ++b)
+      quantize_block_mx(&R[(size_t)b * 32], Wq + (size_t)n * (K / 2) + b * 16,
+                        &w_e8m0[(size_t)n * B + b]);
+  });
 }
 
 svdq_status check_pack_args(const float* W, int N, int K, const float* smooth, uint8_t* Wq,
@@ -425,6 +480,21 @@ svdq_status svdq_quantize_residual(const float* W, int N, int K, const float* sm
     if (st != SVDQ_OK) return st;
     if (r > 0 && (!L1 || !L2)) return fail(SVDQ_ERR_INVALID_ARG, "L1/L2 must not be NULL for r > 0");
     residual_quantize(W, N, K, smooth, L1, L2, r, Wq, w_scales);
+    return SVDQ_OK;
+  } catch (...) {
+    return fail(SVDQ_ERR_INVALID_ARG, "unexpected C++ exception (out of memory?)");
+  }
+}
+
+svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const float* smooth,
+                                         const uint16_t* L1, const uint16_t* L2, int r,
+                                         uint8_t* Wq, uint8_t* w_e8m0) {
+  try {
+    const svdq_status st =
+        check_pack_args(W, N, K, smooth, Wq, reinterpret_cast<float*>(w_e8m0), r);
+    if (st != SVDQ_OK) return st;
+    if (r > 0 && (!L1 || !L2)) return fail(SVDQ_ERR_INVALID_ARG, "L1/L2 must not be NULL for r > 0");
+    residual_quantize_mx(W, N, K, smooth, L1, L2, r, Wq, w_e8m0);
     return SVDQ_OK;
   } catch (...) {
     return fail(SVDQ_ERR_INVALID_ARG, "unexpected C++ exception (out of memory?)");

@@ -40,6 +40,21 @@ Workspace carve_workspace(void* base, int M, int K, int N, int r) {
   return w;
 }
 
+// MXFP4 workspace: qx [M, K/2] | sx [M, K/32] E8M0 bytes | T [slices, M, r].
+MxWorkspace carve_workspace_mx(void* base, int M, int K, int r) {
+  MxWorkspace w;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  const size_t qx_bytes = align256((size_t)M * (K / 2));
+  const size_t sx_bytes = align256((size_t)M * (K / 32));
+  w.t_slices = k1_plan(M, K, r, false).slices;
+  const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
+  w.qx = p;
+  w.sx = p + qx_bytes;
+  w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
+  w.bytes = qx_bytes + sx_bytes + t_bytes;
+  return w;
+}
+
 }  // namespace svdq
 
 using namespace svdq;
@@ -57,6 +72,13 @@ svdq_status check_shapes(int M, int K, int N, int r, bool need_n) {
   if (r < 0 || r > kMaxRank || r % 16 != 0)
     return fail(SVDQ_ERR_INVALID_ARG, "rank must be a multiple of 16 in [0, 128] (got %d)", r);
   return SVDQ_OK;
+}
+
+// MXFP4: the block-scaled MFMA takes 128 channels per step
+svdq_status check_shapes_mx(int M, int K, int N, int r) {
+  if (K < 128 || K % 128 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "K must be a positive multiple of 128 for MXFP4 (got %d)", K);
+  return check_shapes(M, K, N, r, true);
 }
 
 svdq_status check_ptr(const void* p, const char* name, bool may_be_null) {
@@ -197,6 +219,82 @@ svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int 
     return hip_check(
         launch_group_partials(qx, Wq, M, N, K, m0, m1, n0, n1, P, static_cast<hipStream_t>(stream)),
         "group_partials launch");
+  });
+}
+
+size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r) {
+  if (M < 1 || K < 128 || K % 128 || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16) return 0;
+  return carve_workspace_mx(nullptr, M, K, r).bytes;
+}
+
+svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
+                                        const float* smooth, const uint16_t* L1, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, 16, r));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
+                                                      false, static_cast<hipStream_t>(stream)),
+                     "smooth_quant_lora_down (MXFP4) launch");
+  });
+}
+
+svdq_status svdq_forward_gemm_mxfp4(int M, int K, int N, int r, const uint16_t* L2,
+                                    const uint8_t* Wq, const uint8_t* w_e8m0,
+                                    const uint16_t* bias, uint16_t* Y, const void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, N, r));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
+                                       bias, Y, static_cast<hipStream_t>(stream)),
+                     "mxfp4_gemm launch");
+  });
+}
+
+svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                      const float* smooth, const uint16_t* L1,
+                                      const uint16_t* L2, const uint8_t* Wq,
+                                      const uint8_t* w_e8m0, const uint16_t* bias, uint16_t* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, N, r));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
+    SVDQ_TRY(check_ptr(workspace, "workspace", false));
+    const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
+    if (workspace_bytes < w.bytes)
+      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
+                                                        false, s),
+                       "smooth_quant_lora_down (MXFP4) launch"));
+    return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
+                                       bias, Y, s),
+                     "mxfp4_gemm launch");
+  });
+}
+
+svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, const float* smooth,
+                                            const uint16_t* L1, int r, uint8_t* qx,
+                                            uint8_t* sx_e8m0, float* T, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, 16, r));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(check_ptr(qx, "qx", false));
+    SVDQ_TRY(check_ptr(sx_e8m0, "sx_e8m0", false));
+    SVDQ_TRY(check_ptr(T, "T", r == 0));
+    return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, qx, sx_e8m0, T, true,
+                                                      static_cast<hipStream_t>(stream)),
+                     "smooth_quant_lora_down (MXFP4) launch");
   });
 }
 

@@ -28,6 +28,16 @@ struct Workspace {
 };
 Workspace carve_workspace(void* base, int M, int K, int N, int r);
 
+// MXFP4 workspace: qx [M, K/2] | sx [M, K/32] E8M0 bytes | T [slices, M, r].
+struct MxWorkspace {
+  uint8_t* qx;
+  uint8_t* sx;
+  float* T;
+  int t_slices;
+  size_t bytes;
+};
+MxWorkspace carve_workspace_mx(void* base, int M, int K, int r);
+
 // Bytes of fp32 partial accumulators k2 needs for an M x N x K forward.
 size_t gemm_split_bytes(int M, int K, int N);
 
@@ -43,6 +53,11 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice);
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
                                          float* sx, float* T, bool one_slice, hipStream_t stream);
+// The same with MXFP4 codes: qx [M, K/2] E2M1 patterns, sx_e8m0 [M, K/32] bytes.
+hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int r,
+                                            const float* smooth, const uint16_t* L1, uint8_t* qx,
+                                            uint8_t* sx_e8m0, float* T, bool one_slice,
+                                            hipStream_t stream);
 
 // k2: Y = sum_g sx sw P_g + T L2^T + b, bf16 out.  T holds t_slices partial
 // sums of M x r floats, added in order.
@@ -50,6 +65,12 @@ hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, 
                             int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
                             float* part, hipStream_t stream);
+
+// k2, MXFP4 variant: Y = block-scaled FP4 product + T L2^T + b, bf16 out.
+hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, const float* T,
+                             int t_slices, int M, int K, int N, int r, const uint16_t* L2,
+                             const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
+                             uint16_t* Y, hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

@@ -165,6 +165,48 @@ svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const flo
 svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                       int m0, int m1, int n0, int n1, int32_t* P, void* stream);
 
+/* ------------------------------------------------------- MXFP4 variant
+ * The same layer with Q(.) (Terminology Entry, section 2.3, E4) taken as the
+ * OCP microscaling format MXFP4: blocks of 32 consecutive input channels
+ * share one E8M0 scale byte (2^(byte - 127), exponent floor(log2 amax) - 2)
+ * and every element is an FP4 E2M1 number (nearest, ties to even,
+ * saturating at +-6, sign kept).  Codes are packed like the int4 ones (two per
+ * byte, even channel in the low nibble); scales are E8M0 bytes [rows, K/32].
+ * The GEMM runs on CDNA4's block-scaled FP4 MFMA.  Requirements as for the
+ * int4 entry points, with K % 128 == 0. */
+
+/* Stage three with MXFP4 on the host: Wq [N, K/2] and w_e8m0 [N, K/32] of
+ * R = W diag(s) - L2 L1 (R formed exactly as for svdq_quantize_residual). */
+svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const float* smooth,
+                                         const uint16_t* L1, const uint16_t* L2, int r,
+                                         uint8_t* Wq, uint8_t* w_e8m0);
+
+/* Workspace of the MXFP4 forward: codes, E8M0 scales and T; 0 for rejected shapes. */
+size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r);
+
+/* The MXFP4 forward: quantize + lora_down, then the block-scaled GEMM whose
+ * epilogue adds the lora_up product and the bias.  Device memory, asynchronous
+ * on `stream`, no allocation. */
+svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                      const float* smooth, const uint16_t* L1,
+                                      const uint16_t* L2, const uint8_t* Wq,
+                                      const uint8_t* w_e8m0, const uint16_t* bias, uint16_t* Y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Its two halves, as svdq_forward_quantize / svdq_forward_gemm. */
+svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
+                                        const float* smooth, const uint16_t* L1, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+svdq_status svdq_forward_gemm_mxfp4(int M, int K, int N, int r, const uint16_t* L2,
+                                    const uint8_t* Wq, const uint8_t* w_e8m0,
+                                    const uint16_t* bias, uint16_t* Y, const void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Stage 1 into canonical buffers: qx [M, K/2], sx_e8m0 [M, K/32], T [M, r]. */
+svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, const float* smooth,
+                                            const uint16_t* L1, int r, uint8_t* qx,
+                                            uint8_t* sx_e8m0, float* T, void* stream);
+
 const char* svdq_status_string(svdq_status status);
 const char* svdq_last_error(void);
 

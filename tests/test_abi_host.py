@@ -224,3 +224,28 @@ def test_append_lora_bit_exact_with_oracle():
     np.testing.assert_array_equal(L2z, L2o[:, r:])
     with pytest.raises(S.SvdqError):                           # r + rl > 128
         S.svdq_append_lora(s, np.zeros((128, K), np.uint16), np.zeros((N, 128), np.uint16), A, B)
+
+
+@pytest.mark.parametrize("name,rank", [("tiny", 16), ("smallk_640", 32)])
+def test_quantize_residual_mxfp4_bit_exact(name, rank):
+    """The library's MXFP4 residual quantizer gives the oracle's codes and E8M0 bytes
+    from the same s, L1, L2."""
+    w = synth.WORKLOADS[name]
+    W = synth.weight(w)
+    g = np.random.default_rng(6)
+    s = np.exp(g.uniform(-2, 2, w.K)).astype(np.float32)
+    L1 = synth.f32_to_bf16_bits(g.standard_normal((rank, w.K)).astype(np.float32) * 0.05)
+    L2 = synth.f32_to_bf16_bits(g.standard_normal((w.N, rank)).astype(np.float32) * 0.05)
+    Wq, we = S.svdq_quantize_residual_mxfp4(W, s, L1, L2)
+    Wq_o, we_o = O.quantize_residual_mx(W, s, L1, L2)
+    np.testing.assert_array_equal(Wq, Wq_o)
+    np.testing.assert_array_equal(we, we_o)
+
+
+def test_workspace_bytes_mxfp4():
+    al = lambda x: (x + 255) // 256 * 256
+    M, K, N, r = 4096, 3072, 3072, 32
+    b = S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r)
+    assert b == al(M * K // 2) + al(M * K // 32) + al(2 * M * r * 4)
+    assert S.svdq_forward_workspace_bytes_mxfp4(M, 64, N, r) == 0     # K must be a multiple of 128
+    assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 40, r) == 0
