@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E
+PEAK_FP4_TFLOPS = 10100.0   # dense FP4 (and FP6) MFMA
 
 
 def parse():
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--format", choices=["int4", "mxfp4"], default="int4",
+                    help="int4: symmetric int4, one fp32 scale per 64 channels (int8 MFMA); "
+                         "mxfp4: E2M1 with an E8M0 scale per 32 (block-scaled FP4 MFMA)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps replayed from a HIP graph; value is then the graph rate")
     return ap.parse_args()
@@ -106,6 +110,9 @@ def main():
     A = np.zeros(K, np.float32)
     S.svdq_act_absmax_update(synth.calibration_activations(w), A)
     pk = S.svdq_pack_weights(W, A, w.alpha, r)
+    mx = args.format == "mxfp4"
+    if mx:   # same s, L1, L2; the residual quantized to MXFP4
+        pk["Wq"], pk["w_scales"] = S.svdq_quantize_residual_mxfp4(W, pk["smooth"], pk["L1"], pk["L2"])
     pack_s = time.time() - t0
     print(f"# packed {args.workload} in {pack_s:.1f}s", file=sys.stderr, flush=True)
 
@@ -113,8 +120,9 @@ def main():
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    per_set = (M * K * 2 + M * N * 2 + S.svdq_forward_workspace_bytes(M, K, N, r)
-               + N * K // 2 + N * K // 64 * 4 + r * (K + N) * 2 + K * 4 + N * 2)
+    ws_bytes = (S.svdq_forward_workspace_bytes_mxfp4 if mx else S.svdq_forward_workspace_bytes)(M, K, N, r)
+    per_set = (M * K * 2 + M * N * 2 + ws_bytes + N * K // 2 + pk["w_scales"].nbytes
+               + r * (K + N) * 2 + K * 4 + N * 2)
     nsets = max(2, -(-args.rotate_mb * (1 << 20) // per_set))
     sets = []
     base = dict(X=t(X), s=t(pk["smooth"]), L1=t(pk["L1"]), L2=t(pk["L2"]), Wq=t(pk["Wq"]),
@@ -122,13 +130,16 @@ def main():
     for i in range(nsets):
         d = {k: v.clone() for k, v in base.items()}
         d["Y"] = torch.empty((M, N), dtype=torch.int16, device=dev)
-        d["work"] = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=dev)
+        d["work"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         sets.append(d)
     torch.cuda.synchronize()
 
+    quantize = S.svdq_forward_quantize_mxfp4 if mx else S.svdq_forward_quantize
+    gemm = S.svdq_forward_gemm_mxfp4 if mx else S.svdq_forward_gemm
+
     def step(d):
-        S.svdq_forward_quantize(d["X"], d["s"], d["L1"], d["work"])
-        S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+        quantize(d["X"], d["s"], d["L1"], d["work"])
+        gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -146,9 +157,9 @@ def main():
         d = sets[i % nsets]
         e = ev[i]
         e[0].record()
-        S.svdq_forward_quantize(d["X"], d["s"], d["L1"], d["work"])
+        quantize(d["X"], d["s"], d["L1"], d["work"])
         e[1].record()
-        S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+        gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
         e[2].record()
     end.record()
     torch.cuda.synchronize()
@@ -187,25 +198,31 @@ def main():
         graph_info = {"replays": replays, "steps_per_graph": nsets, "ms_per_step": round(ms_step, 5),
                       "eager_ms_per_step": round(eager_ms_step, 5)}
 
-    ops_main = 2.0 * M * N * K                 # int8 MFMA work of the W4A4 product
+    ops_main = 2.0 * M * N * K                 # the 4-bit product (int8 or FP4 MFMA)
     ops_low = 2.0 * M * r * (K + N)            # bf16 low-rank branch
     tops = (ops_main + ops_low) / (ms_step * 1e-3) / 1e12
     tokens_s = M / (ms_step * 1e-3)
-    k1_bytes = M * (2 * K + K // 2 + 4 * (K // 64) + 4 * r) + r * K * 2 + K * 4
-    k2_bytes = (M * (K // 2 + 4 * (K // 64) + 4 * r + 2 * N)
-                + N * K // 2 + 4 * N * (K // 64) + 2 * r * (K + N) + 2 * N)
+    # scale bytes per row: one fp32 per 64 channels (int4) or one E8M0 byte per 32 (mxfp4)
+    sb_row = K // 32 if mx else 4 * (K // 64)
+    k1_bytes = M * (2 * K + K // 2 + sb_row + 4 * r) + r * K * 2 + K * 4
+    k2_bytes = (M * (K // 2 + sb_row + 4 * r + 2 * N)
+                + N * K // 2 + N * sb_row + 2 * r * (K + N) + 2 * N)
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
+    peak_mfma = PEAK_FP4_TFLOPS if mx else PEAK_INT8_TOPS
     # k2's bound: whichever roofline floor is longer at this shape
-    k2_bound = "mfma" if ops_main / (PEAK_INT8_TOPS * 1e12) >= k2_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"
+    k2_bound = "mfma" if ops_main / (peak_mfma * 1e12) >= k2_bytes / (PEAK_HBM_GBS * 1e9) else "hbm"
     if k2_bound == "mfma":
-        k2_achieved, k2_peak, k2_unit = ops_main / (k2_ms * 1e-3) / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
+        k2_achieved, k2_peak, k2_unit = ops_main / (k2_ms * 1e-3) / 1e12, peak_mfma, "TFLOP/s"
     else:
         k2_achieved, k2_peak, k2_unit = k2_bytes / (k2_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     k2_tops = ops_main / (k2_ms * 1e-3) / 1e12
-    if args.workload == "dit_proj":
+    kind = "MXFP4" if mx else "W4A4"
+    if args.workload == "dit_proj" and not mx:
         metric = "fused W4A4+low-rank linear TOPS and tokens/s at M=4096,K=N=3072,r=32 (% MFMA peak)"
     else:
-        metric = f"fused W4A4+low-rank linear TOPS and tokens/s at M={M},K={K},N={N},r={r} (% MFMA peak)"
+        metric = f"fused {kind}+low-rank linear TOPS and tokens/s at M={M},K={K},N={N},r={r} (% MFMA peak)"
+    k1_file, k2_file = ("k1_smooth_quant.hip", "k2_mxfp4_gemm.hip") if mx else \
+        ("k1_smooth_quant.hip", "k2_w4a4_gemm.hip")
 
     out = {
         "metric": metric,
@@ -218,33 +235,34 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output",
+        "dtype": ("fp4 e2m1 + e8m0 block scales on block-scaled FP4 MFMA (fp32 acc), bf16 low-rank + output"
+                  if mx else "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output"),
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "rank": r, "group": 64,
-                   "rotated_sets": nsets, "hip_graph": bool(args.graph)},
+        "config": {"workload": args.workload, "format": args.format, "M": M, "K": K, "N": N, "rank": r,
+                   "group": 32 if mx else 64, "rotated_sets": nsets, "hip_graph": bool(args.graph)},
         "tokens_per_s": round(tokens_s, 1),
-        "pct_int8_mfma_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "pct_mfma_peak": round(100.0 * tops / peak_mfma, 2),
         "roofline": {
-            "kernel": "w4a4_gemm (k2)",
+            "kernel": "mxfp4_gemm (k2)" if mx else "w4a4_gemm (k2)",
             "bound": k2_bound,
             "achieved": round(k2_achieved, 2),
             "peak": k2_peak,
             "unit": k2_unit,
             "frac": round(k2_achieved / k2_peak, 4),
-            "algorithmic": {"int8_ops": ops_main, "bytes": k2_bytes},
-            "traffic": load_traffic("k2_w4a4_gemm.hip", args.workload),
+            "algorithmic": {"ops": ops_main, "bytes": k2_bytes},
+            "traffic": load_traffic(k2_file, args.workload + ("_mxfp4" if mx else "")),
             "avg_launch_us": round(k2_ms * 1e3, 3),
         },
         "kernels": {
             "k1_smooth_quant_lora_down": {"avg_launch_us": round(k1_ms * 1e3, 3), "bound": "hbm",
                                           "algorithmic_bytes": k1_bytes, "achieved_GBs": round(k1_gbs, 1),
                                           "peak_GBs": PEAK_HBM_GBS, "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
-                                          "traffic": load_traffic("k1_smooth_quant.hip", args.workload)},
-            "k2_w4a4_gemm": {"avg_launch_us": round(k2_ms * 1e3, 3), "int8_ops": ops_main,
-                             "achieved_TOPS": round(k2_tops, 2),
-                             "pct_int8_peak": round(100.0 * k2_tops / PEAK_INT8_TOPS, 2),
-                             "algorithmic_bytes": k2_bytes,
-                             "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)},
+                                          "traffic": load_traffic(k1_file, args.workload + ("_mxfp4" if mx else ""))},
+            "k2_gemm": {"avg_launch_us": round(k2_ms * 1e3, 3), "ops": ops_main,
+                        "achieved_TOPS": round(k2_tops, 2),
+                        "pct_mfma_peak": round(100.0 * k2_tops / peak_mfma, 2),
+                        "algorithmic_bytes": k2_bytes,
+                        "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)},
         },
         "graph": graph_info,
         "wall_s_timed": round(wall, 4),
@@ -252,11 +270,11 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds, mx)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, X, pk, b, seconds):
+def cpu_baseline(w, X, pk, b, seconds, mx=False):
     """The CPU oracle (as it stands) on a bounded sample of rows of the same workload."""
     from oracle import svdq_oracle as O
     try:
@@ -264,12 +282,13 @@ def cpu_baseline(w, X, pk, b, seconds):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = 1
+    fwd = O.forward_mx if mx else O.forward
     # grow the sample until it takes about `seconds` (whole workload, repeated, if it is smaller)
     rows, passes, dt = 16, 1, 0.0
     for _ in range(6):
         t0 = time.perf_counter()
         for _ in range(passes):
-            O.forward(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
+            fwd(X[:rows], pk["smooth"], pk["L1"], pk["L2"], pk["Wq"], pk["w_scales"], b)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * seconds or passes >= 8:
             break

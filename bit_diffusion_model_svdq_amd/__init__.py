@@ -22,6 +22,15 @@ LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with python bit_diffusion_model_svdq_amd/build.py")
 
+# torch ships its own HIP runtime under the same soname as the system one the
+# library is linked against.  Whichever is loaded first serves the whole
+# process, and a process that ends up with parts of both finds no device, so
+# torch (which owns the device memory and streams) is loaded before the library.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # host-only use (packer) without torch
+    _torch = None
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 SVDQ_OK = 0

@@ -21,18 +21,15 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
 // acc[tm][tn] holds the 16x16 tile (wr + 16 tm, wc + 16 tn) of the block's
 // BM x BN output in the MFMA result layout (lane l: column l % 16, rows
 // 4 (l / 16) + i).  T holds t_slices partial sums of M x r floats, t_stride
-// floats apart, added in slice order.  T is split into a bf16 hi/lo pair and
-// enters bf16 MFMAs whose accumulator input is the tile, so the branch keeps
-// ~16 significant bits of T.  lds must hold BM * BN * 2 bytes; the caller has
-// synchronized the block so that the space is free.
-template <int TM, int TN, int BM, int BN, int THREADS>
-__device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
+// floats apart, added in slice order.  T (times `scale`, a power of two) is
+// split into a bf16 hi/lo pair and enters bf16 MFMAs whose accumulator input
+// is the tile, so the branch keeps ~16 significant bits of T.
+template <int TM, int TN>
+__device__ inline void lowrank_accumulate(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
                                           int t_slices, long t_stride, int r,
-                                          const uint16_t* __restrict__ L2,
-                                          const uint16_t* __restrict__ bias,
-                                          uint16_t* __restrict__ Y, int ldy, int m0, int n0,
-                                          int row1, int col1, int wr, int wc, int lane, int tid,
-                                          uint8_t* lds) {
+                                          const uint16_t* __restrict__ L2, int m0, int n0,
+                                          int row1, int col1, int wr, int wc, int lane,
+                                          float scale) {
   const int fr = lane & 15;
   const int fk = lane >> 4;
   for (int j0 = 0; j0 < r; j0 += 32) {
@@ -53,8 +50,8 @@ __device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __r
           a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
           b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
         }
-        tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
-        tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
+        tv[0] = a.x * scale; tv[1] = a.y * scale; tv[2] = a.z * scale; tv[3] = a.w * scale;
+        tv[4] = b.x * scale; tv[5] = b.y * scale; tv[6] = b.z * scale; tv[7] = b.w * scale;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) tv[e] = 0.f;
@@ -79,6 +76,17 @@ __device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __r
       }
     }
   }
+}
+
+// Bias, bf16 rounding and the store of the tile through LDS as 16-byte row
+// segments.  lds must hold BM * BN * 2 bytes; the caller has synchronized the
+// block so that the space is free.
+template <int TM, int TN, int BM, int BN, int THREADS>
+__device__ inline void bias_store(f32x4 (&acc)[TM][TN], const uint16_t* __restrict__ bias,
+                                  uint16_t* __restrict__ Y, int ldy, int m0, int n0, int row1,
+                                  int col1, int wr, int wc, int lane, int tid, uint8_t* lds) {
+  const int fr = lane & 15;
+  const int fk = lane >> 4;
 
   // bias, bf16, then the tile goes through LDS (columns swizzled by 16 elements
   // per group of 4 rows, so that the 4 row groups of a write hit distinct banks)
@@ -108,6 +116,26 @@ __device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __r
       *reinterpret_cast<uint4*>(Y + (size_t)m * ldy + n) = v;
     }
   }
+}
+
+}  // namespace tail
+}  // namespace svdq
+
+namespace svdq {
+namespace tail {
+
+template <int TM, int TN, int BM, int BN, int THREADS>
+__device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
+                                          int t_slices, long t_stride, int r,
+                                          const uint16_t* __restrict__ L2,
+                                          const uint16_t* __restrict__ bias,
+                                          uint16_t* __restrict__ Y, int ldy, int m0, int n0,
+                                          int row1, int col1, int wr, int wc, int lane, int tid,
+                                          uint8_t* lds) {
+  lowrank_accumulate<TM, TN>(acc, T, t_slices, t_stride, r, L2, m0, n0, row1, col1, wr, wc, lane,
+                             1.0f);
+  bias_store<TM, TN, BM, BN, THREADS>(acc, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
+                                      lds);
 }
 
 }  // namespace tail

@@ -24,10 +24,13 @@
 // fragments and scales of the stage, then issues its copies of the next stage,
 // then runs the stage's 2 x TM x TN MFMAs while the copies travel.
 //
-// The 16-byte chunks of a row are XOR-swizzled by (row / 2) % 8, so that the
-// 16 rows of a fragment read land in 16 distinct bank groups; the direct copy
+// The 16-byte chunks of a row are XOR-swizzled (see swz_key); the direct copy
 // writes lane-linear LDS addresses, so each lane fetches the global chunk that
 // belongs at its LDS position.
+//
+// The low-rank branch's up projection T L2^T initializes the accumulators
+// before the main loop (its loads travel with the first stage's copies), so
+// that only the bias and the store are left after it.
 #include "gemm_tail.h"
 #include "svdq_internal.h"
 
@@ -81,8 +84,13 @@ __device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
   tn = in / gsize;
 }
 
-// physical 16-byte chunk of logical chunk c in LDS row `row`
-__device__ inline int swz(int row, int c) { return row * ROWB + ((c ^ ((row >> 1) & 7)) << 4); }
+// The 8 chunks of a 128-byte row are XOR-swizzled by row % 8.  A fragment read
+// spans 16 consecutive rows starting at a multiple of 16, so the key depends on
+// the lane alone and every fragment of a wave shares one base address plus
+// immediate offsets; the LDS reports no bank conflicts for this pattern.
+__device__ inline int swz_key(int row) { return row & 7; }
+// byte offset of logical 16-byte chunk c of LDS row `row`
+__device__ inline int swz(int row, int c) { return row * ROWB + ((c ^ swz_key(row)) << 4); }
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     const int jrow = lane >> 3, pch = lane & 7;
     for (int q = wave; q < bytes / 1024; q += C::WAVES) {
       const int row = q * (1024 / ROWB) + jrow;
-      int chunk = pch ^ ((row >> 1) & 7);
+      int chunk = pch ^ swz_key(row);
       if (s * SK + (chunk >> 2) >= ksteps) chunk &= 3;
       const uint8_t* g = src + (size_t)min(row_base + row, nrows_total - 1) * ld + s * ROWB + chunk * 16;
       __builtin_amdgcn_global_load_lds(g, (lds_ptr)(dst + q * 1024), 16, 0, 0);
@@ -203,6 +211,8 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   };
 
   copy_stage(0, 0);
+  tail::lowrank_accumulate<C::TM, C::TN>(acc, T, t_slices, t_stride, r, L2, m0, n0, M, N, wr, wc,
+                                         lane, 1.0f);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int s = 0; s < stages; ++s) {
@@ -211,8 +221,8 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     __syncthreads();                 // ... and everyone's; the current buffer is free
   }
 
-  tail::lowrank_bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
-      acc, T, t_slices, t_stride, r, L2, bias, Y, N, m0, n0, M, N, wr, wc, lane, tid, lds);
+  tail::bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(acc, bias, Y, N, m0, n0, M, N, wr, wc,
+                                                           lane, tid, lds);
 }
 
 int cu_count_mx() {
