@@ -308,12 +308,37 @@ def group_partials(qx_packed, wq_packed) -> np.ndarray:
     return P
 
 
-def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
+# ------------------------------------------------ MLP activation (DiT block)
+# A DiT MLP puts GELU between its up and down projections.  GELU in its tanh
+# form (Hendrycks and Gimpel, "Gaussian Error Linear Units", section 2):
+#   gelu(x) = 0.5 x (1 + tanh(sqrt(2 / pi) (x + 0.044715 x^3))).
+# The pages do not treat the MLP; the reading used here fuses the activation
+# into the up projection's output: gelu of the float sum main + low + b,
+# before the output's single rounding to bfloat16.
+ACTIVATIONS = (None, "gelu_tanh")
+
+
+def gelu_tanh(x) -> np.ndarray:
+    """GELU, tanh form, in float64."""
+    x = np.asarray(x, dtype=F64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _activate(Y, activation):
+    if activation is None:
+        return Y
+    if activation == "gelu_tanh":
+        return gelu_tanh(Y)
+    raise ValueError(f"unknown activation {activation!r}")
+
+
+def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None, activation=None):
     """Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1^T) L2^T + b in float64.
 
     [Term] 2.3 (E4) and (E7); bias added once.  The low-bit term is
     sum_g sx[m, g] * sw[n, g] * P[m, n, g] with exact integer P.
-    Returns float64 [M, N].
+    activation "gelu_tanh" applies gelu_tanh to the sum (the MLP's up
+    projection).  Returns float64 [M, N].
     """
     qx, sx, T, _ = quantize_activations(X_bf16, s, L1_bf16)
     qxv = unpack_nibbles(qx).astype(F64)
@@ -334,7 +359,7 @@ def forward(X_bf16, s, L1_bf16, L2_bf16, Wq, w_scales, bias_bf16=None):
     Y = main + low
     if bias_bf16 is not None:
         Y = Y + bf16_to_f64(bias_bf16)[None, :]
-    return Y
+    return _activate(Y, activation)
 
 
 def append_lora(s, L1_bf16, L2_bf16, A, B):
@@ -463,7 +488,7 @@ def quantize_activations_mx(X_bf16, s, L1_bf16=None):
     return pack_nibbles(codes.astype(np.int64)), e8m0_bytes(e), T, xh
 
 
-def forward_mx(X_bf16, s, L1_bf16, L2_bf16, Wq, w_e8m0, bias_bf16=None):
+def forward_mx(X_bf16, s, L1_bf16, L2_bf16, Wq, w_e8m0, bias_bf16=None, activation=None):
     """Y = Q_mx(X diag(s)^-1) Q_mx(R) + (X diag(s)^-1 L1^T) L2^T + b in float64.
 
     The low-bit term is sum over blocks b of 2^(ea[m,b] + eb[n,b]) times the
@@ -484,7 +509,7 @@ def forward_mx(X_bf16, s, L1_bf16, L2_bf16, Wq, w_e8m0, bias_bf16=None):
     Y = main + low
     if bias_bf16 is not None:
         Y = Y + bf16_to_f64(bias_bf16)[None, :]
-    return Y
+    return _activate(Y, activation)
 
 
 def rel_fro(Y, Yref) -> float:

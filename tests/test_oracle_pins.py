@@ -550,3 +550,56 @@ def test_mx_forward_matches_exact_rationals():
                 sl = slice(32 * blk, 32 * blk + 32)
                 acc += sum(a * w for a, w in zip(q_block(xv[m, sl]), q_block(W[n, sl])))
             assert Fr(Y[m, n]) == acc
+
+
+# ------------------------------------------------------------- GELU (tanh form)
+def test_gelu_tanh_odd_part_is_identity():
+    """0.5 x (1 + tanh u(x)) - 0.5 (-x) (1 + tanh u(-x)) = x because u is odd and tanh is odd:
+    a dropped 1/2, a sign error inside u or a missing x fails this."""
+    x = np.linspace(-9.0, 9.0, 3601)
+    d = O.gelu_tanh(x) - O.gelu_tanh(-x)
+    assert np.max(np.abs(d - x)) <= 1e-14 * 9.0
+
+
+def test_gelu_tanh_against_erf_gelu():
+    """The tanh form approximates x Phi(x) (Phi from math.erf, a library routine) to
+    within 4.8e-4 everywhere; a wrong cubic coefficient (0.04 or 0.05) or a wrong
+    sqrt(2/pi) (0.8) gives 6e-4 to 3e-3."""
+    x = np.linspace(-8.0, 8.0, 16001)
+    exact = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    err = np.abs(O.gelu_tanh(x) - exact)
+    assert err.max() <= 4.8e-4
+    assert err.max() >= 1e-4          # it is the tanh form, not the erf form
+    assert np.abs(x[np.argmax(err)]) > 2.0 and np.abs(x[np.argmax(err)]) < 3.5
+
+
+def test_gelu_tanh_limits_and_minimum():
+    assert O.gelu_tanh(0.0) == 0.0
+    assert abs(O.gelu_tanh(20.0) - 20.0) < 1e-12
+    assert abs(O.gelu_tanh(-20.0)) < 1e-12
+    # slope 1/2 at the origin
+    h = 1e-6
+    assert abs((O.gelu_tanh(h) - O.gelu_tanh(-h)) / (2 * h) - 0.5) < 1e-9
+    # the minimum, about -0.17 near x = -0.75 (GELU's known shape)
+    x = np.linspace(-3.0, 0.0, 30001)
+    g = O.gelu_tanh(x)
+    assert -0.171 < g.min() < -0.169 and -0.80 < x[np.argmin(g)] < -0.70
+
+
+def test_forward_activation_is_applied_after_bias():
+    """The fused point: gelu of main + low + b (bias included), unknown names rejected."""
+    rng = np.random.default_rng(7)
+    M, K, N, r = 4, 128, 16, 16
+    X = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    s = np.ones(K, np.float32)
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    L1 = O.bf16_from_f64(rng.standard_normal((r, K)) * 0.05)
+    L2 = O.bf16_from_f64(rng.standard_normal((N, r)) * 0.05)
+    Wq, sw = O.quantize_residual(W, s, L1, L2)
+    b = O.bf16_from_f64(rng.standard_normal(N))
+    Y = O.forward(X, s, L1, L2, Wq, sw, b)
+    Yg = O.forward(X, s, L1, L2, Wq, sw, b, activation="gelu_tanh")
+    assert np.array_equal(O.gelu_tanh(Y), Yg)
+    assert not np.allclose(Yg, O.gelu_tanh(Y - O.bf16_to_f64(b)[None, :]) + O.bf16_to_f64(b)[None, :])
+    with pytest.raises(ValueError):
+        O.forward(X, s, L1, L2, Wq, sw, b, activation="relu")
