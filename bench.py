@@ -11,6 +11,11 @@ Prints one JSON line (rank 0).  Default workload: the DiT attention
 projection, M=4096 tokens, K=N=3072, rank 32.  Other workloads (--workload)
 are the small-K UNet widths and the DiT MLP linears; --graph replays whole
 rotations of steps from a HIP graph (for the launch-bound small shapes).
+--workload dit_block times the four SVDQuant linears of a DiT block at width
+3072 and 4608 tokens (fused QKV 3072 -> 9216, attention output 3072 -> 3072,
+MLP up 3072 -> 12288 with GELU fused into its epilogue, MLP down
+12288 -> 3072 reading the up projection's output), each branch widened by a
+seeded rank-16 LoRA to r = 48; the attention itself is not part of it.
 """
 from __future__ import annotations
 
@@ -98,6 +103,8 @@ def main():
     import bit_diffusion_model_svdq_amd as S
     import synth
 
+    if args.workload == "dit_block":
+        return bench_block(args, S, synth, torch)
     w = synth.WORKLOADS[args.workload]
     M, K, N, r = w.M, w.K, w.N, w.rank
     dev = torch.device("cuda:0")
@@ -272,6 +279,178 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds, mx)
     print(json.dumps(out), flush=True)
+
+
+# The DiT block: (name, workload, activation, input); "H" is the up projection's output.
+BLOCK = (("qkv", "dit_qkv", "none", "X"), ("out", "dit_out", "none", "X"),
+         ("up", "mlp_up", "gelu_tanh", "X"), ("down", "mlp_down", "none", "H"))
+
+
+def bench_block(args, S, synth, torch):
+    mx = args.format == "mxfp4"
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    # ---- offline pack of the four layers (host, untimed): library packer, LoRA appended
+    t0 = time.time()
+    layers = []
+    for name, wname, act, src in BLOCK:
+        w = synth.WORKLOADS[wname]
+        W = synth.weight(w)
+        A = np.zeros(w.K, np.float32)
+        S.svdq_act_absmax_update(synth.calibration_activations(w), A)
+        pk = S.svdq_pack_weights(W, A, w.alpha, w.rank)
+        if mx:
+            pk["Wq"], pk["w_scales"] = S.svdq_quantize_residual_mxfp4(W, pk["smooth"], pk["L1"], pk["L2"])
+        la, lb = synth.lora_factors(w)
+        L1, L2 = S.svdq_append_lora(pk["smooth"], pk["L1"], pk["L2"], la, lb)
+        X = synth.activations(w) if src == "X" else None
+        layers.append(dict(name=name, w=w, act=act, src=src, M=w.M, K=w.K, N=w.N, r=L1.shape[0], X=X,
+                           pk=dict(pk, L1=L1, L2=L2), b=synth.bias(w)))
+    pack_s = time.time() - t0
+    print(f"# packed dit_block in {pack_s:.1f}s", file=sys.stderr, flush=True)
+    M = layers[0]["M"]
+    assert all(L["M"] == M for L in layers)
+
+    wsb = S.svdq_forward_workspace_bytes_mxfp4 if mx else S.svdq_forward_workspace_bytes
+    quantize = S.svdq_forward_quantize_mxfp4 if mx else S.svdq_forward_quantize
+    gemm = S.svdq_forward_gemm_act_mxfp4 if mx else S.svdq_forward_gemm_act
+    acts = {"none": S.SVDQ_ACT_NONE, "gelu_tanh": S.SVDQ_ACT_GELU_TANH}
+    per_set = 0
+    for L in layers:
+        L["ws_bytes"] = wsb(L["M"], L["K"], L["N"], L["r"])
+        per_set += (L["M"] * L["K"] * 2 if L["X"] is not None else 0) + L["M"] * L["N"] * 2 + L["ws_bytes"] \
+            + L["N"] * L["K"] // 2 + L["pk"]["w_scales"].nbytes + L["r"] * (L["K"] + L["N"]) * 2
+    nsets = max(2, -(-args.rotate_mb * (1 << 20) // per_set))
+    sets = []
+    for i in range(nsets):
+        d = []
+        for L in layers:
+            e = dict(s=t(L["pk"]["smooth"]), L1=t(L["pk"]["L1"]), L2=t(L["pk"]["L2"]), Wq=t(L["pk"]["Wq"]),
+                     ws=t(L["pk"]["w_scales"]), b=t(L["b"]),
+                     Y=torch.empty((L["M"], L["N"]), dtype=torch.int16, device=dev),
+                     work=torch.empty(L["ws_bytes"], dtype=torch.uint8, device=dev))
+            e["X"] = t(L["X"]) if L["X"] is not None else None
+            d.append(e)
+        d[3]["X"] = d[2]["Y"]          # the down projection reads H = GELU(up) in place
+        sets.append(d)
+    torch.cuda.synchronize()
+
+    def run(d, ev=None):
+        for j, (L, e) in enumerate(zip(layers, d)):
+            if ev is not None:
+                ev[2 * j].record()
+            quantize(e["X"], e["s"], e["L1"], e["work"])
+            if ev is not None:
+                ev[2 * j + 1].record()
+            gemm(L["M"], L["K"], e["L2"], e["Wq"], e["ws"], e["b"], acts[L["act"]], e["Y"], e["work"], L["r"])
+        if ev is not None:
+            ev[2 * len(layers)].record()
+
+    for i in range(args.warmup):
+        run(sets[i % nsets])
+    torch.cuda.synchronize()
+    nev = 2 * len(layers) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run(sets[i % nsets], evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs]).mean(axis=0)
+
+    peak_mfma = PEAK_FP4_TFLOPS if mx else PEAK_INT8_TOPS
+    sb_row = lambda K: K // 32 if mx else 4 * (K // 64)
+    kern = {}
+    ops_total = 0.0
+    for j, L in enumerate(layers):
+        M_, K, N, r = L["M"], L["K"], L["N"], L["r"]
+        ops_main, ops_low = 2.0 * M_ * N * K, 2.0 * M_ * r * (K + N)
+        ops_total += ops_main + ops_low
+        k1_ms, k2_ms = float(dur[2 * j]), float(dur[2 * j + 1])
+        k1_bytes = M_ * (2 * K + K // 2 + sb_row(K) + 4 * r) + r * K * 2 + K * 4
+        k2_bytes = (M_ * (K // 2 + sb_row(K) + 4 * r + 2 * N) + N * K // 2 + N * sb_row(K)
+                    + 2 * r * (K + N) + 2 * N)
+        kern[L["name"]] = {
+            "M": M_, "K": K, "N": N, "r": r, "activation": L["act"],
+            "k1_us": round(k1_ms * 1e3, 3), "k1_GBs": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
+            "k2_us": round(k2_ms * 1e3, 3), "k2_ops": ops_main, "k2_bytes": k2_bytes,
+            "k2_TOPS": round(ops_main / (k2_ms * 1e-3) / 1e12, 2),
+            "k2_pct_mfma_peak": round(100.0 * ops_main / (k2_ms * 1e-3) / 1e12 / peak_mfma, 2)}
+    dom = max(kern, key=lambda k: kern[k]["k2_us"])
+    dk = kern[dom]
+    achieved = dk["k2_ops"] / (dk["k2_us"] * 1e-6) / 1e12
+    tops = ops_total / (ms_step * 1e-3) / 1e12
+    kind = "MXFP4" if mx else "W4A4"
+    out = {
+        "metric": (f"fused {kind}+low-rank DiT block (QKV 3072->9216, out 3072->3072, MLP 3072->12288 +GELU "
+                   f"->3072; r=32+16 LoRA) TOPS and tokens/s at M={M} (% MFMA peak)"),
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("fp4 e2m1 + e8m0 block scales on block-scaled FP4 MFMA (fp32 acc), bf16 low-rank + output"
+                  if mx else "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output"),
+        "data": "synthetic",
+        "config": {"workload": "dit_block", "format": args.format, "M": M, "layers": [L["name"] for L in layers],
+                   "rank": layers[0]["r"], "rotated_sets": nsets},
+        "tokens_per_s": round(M / (ms_step * 1e-3), 1),
+        "pct_mfma_peak": round(100.0 * tops / peak_mfma, 2),
+        "roofline": {"kernel": f"{'mxfp4' if mx else 'w4a4'}_gemm (k2) of the {dom} projection", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak_mfma, 4),
+                     "algorithmic": {"ops": dk["k2_ops"], "bytes": dk["k2_bytes"]}, "traffic": None,
+                     "avg_launch_us": dk["k2_us"]},
+        "kernels": kern,
+        "wall_s_timed": round(wall, 4),
+        "pack_s": round(pack_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(layers, args.cpu_seconds, mx)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_block(layers, seconds, mx):
+    """The CPU oracle on the same few token rows through the four layers (its own chain)."""
+    from oracle import svdq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    fwd = O.forward_mx if mx else O.forward
+    rows, dt = 4, 0.0
+    for _ in range(5):
+        t0 = time.perf_counter()
+        H = None
+        for L in layers:
+            X = L["X"][:rows] if L["src"] == "X" else O.bf16_from_f64(H)
+            Y = fwd(X, L["pk"]["smooth"], L["pk"]["L1"], L["pk"]["L2"], L["pk"]["Wq"], L["pk"]["w_scales"],
+                    L["b"], activation=None if L["act"] == "none" else L["act"])
+            if L["name"] == "up":
+                H = Y
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * seconds or rows >= 256:
+            break
+        rows = int(min(256, max(rows + 1, rows * min(8.0, 1.2 * seconds / max(dt, 1e-3)))))
+    ops = sum(2.0 * rows * L["N"] * L["K"] + 2.0 * rows * L["r"] * (L["K"] + L["N"]) for L in layers)
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(rows / dt, 2),
+            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": (f"{rows} token rows through the four block linears (full K and N, r=48), float64 numpy "
+                       f"oracle chain on host cores")}
 
 
 def cpu_baseline(w, X, pk, b, seconds, mx=False):

@@ -45,7 +45,13 @@ EXPORTS = [
     "svdq_status_string", "svdq_last_error",
     "svdq_quantize_residual_mxfp4", "svdq_forward_workspace_bytes_mxfp4", "svdq_linear_forward_mxfp4",
     "svdq_forward_quantize_mxfp4", "svdq_forward_gemm_mxfp4", "svdq_quantize_activations_mxfp4",
+    "svdq_linear_forward_act", "svdq_forward_gemm_act", "svdq_linear_forward_act_mxfp4",
+    "svdq_forward_gemm_act_mxfp4",
 ]
+
+# svdq_activation
+SVDQ_ACT_NONE = 0
+SVDQ_ACT_GELU_TANH = 1
 
 
 class SvdqError(RuntimeError):
@@ -79,6 +85,10 @@ _sig = {
     "svdq_forward_quantize_mxfp4": [_P, _I, _I, _I, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_forward_gemm_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_quantize_activations_mxfp4": [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P],
+    "svdq_linear_forward_act": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_gemm_act": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
+    "svdq_linear_forward_act_mxfp4": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
+    "svdq_forward_gemm_act_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "svdq_status_string": [_I],
     "svdq_last_error": [],
 }
@@ -202,6 +212,19 @@ def svdq_linear_forward(X, smooth, L1, L2, Wq, w_scales, bias, Y, workspace, str
     return Y
 
 
+def svdq_linear_forward_act(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y, workspace,
+                            stream=None):
+    """svdq_linear_forward with an svdq_activation applied to Y (SVDQ_ACT_GELU_TANH: GELU, tanh form)."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_linear_forward_act(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                      _dp(w_scales), _dp(bias), int(activation), _dp(Y), _dp(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_linear_forward_act")
+    return Y
+
+
 def svdq_forward_quantize(X, smooth, L1, workspace, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
@@ -216,6 +239,14 @@ def svdq_forward_gemm(M, K, L2, Wq, w_scales, bias, Y, workspace, r, stream=None
                                 _dp(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream))
     _check(st, "svdq_forward_gemm")
+
+
+def svdq_forward_gemm_act(M, K, L2, Wq, w_scales, bias, activation, Y, workspace, r, stream=None):
+    N = Wq.shape[0]
+    st = _lib.svdq_forward_gemm_act(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_scales), _dp(bias),
+                                    int(activation), _dp(Y), _dp(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_forward_gemm_act")
 
 
 def svdq_quantize_activations(X, smooth, L1, qx, sx, T, stream=None):
@@ -275,6 +306,19 @@ def svdq_linear_forward_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, Y, workspace,
     return Y
 
 
+def svdq_linear_forward_act_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, activation, Y, workspace,
+                                  stream=None):
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = L1.shape[0] if L1 is not None else 0
+    st = _lib.svdq_linear_forward_act_mxfp4(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2),
+                                            _dp(Wq), _dp(w_e8m0), _dp(bias), int(activation), _dp(Y),
+                                            _dp(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream))
+    _check(st, "svdq_linear_forward_act_mxfp4")
+    return Y
+
+
 def svdq_forward_quantize_mxfp4(X, smooth, L1, workspace, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
@@ -289,6 +333,15 @@ def svdq_forward_gemm_mxfp4(M, K, L2, Wq, w_e8m0, bias, Y, workspace, r, stream=
                                       _dp(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream))
     _check(st, "svdq_forward_gemm_mxfp4")
+
+
+def svdq_forward_gemm_act_mxfp4(M, K, L2, Wq, w_e8m0, bias, activation, Y, workspace, r,
+                                stream=None):
+    N = Wq.shape[0]
+    st = _lib.svdq_forward_gemm_act_mxfp4(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_e8m0), _dp(bias),
+                                          int(activation), _dp(Y), _dp(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "svdq_forward_gemm_act_mxfp4")
 
 
 def svdq_quantize_activations_mxfp4(X, smooth, L1, qx, sx_e8m0, T, stream=None):

@@ -1,7 +1,8 @@
 // Shared tail of the two GEMM kernels (int4 and MXFP4): adds the low-rank
 // branch's up projection T L2^T (Terminology Entry, section 2.3, E4 second
-// term) and the bias to a finished fp32 output tile, rounds to bf16 and
-// stores the tile through LDS as 16-byte row segments.
+// term) and the bias to a finished fp32 output tile, optionally applies the
+// MLP activation, rounds to bf16 and stores the tile through LDS as 16-byte
+// row segments.
 #pragma once
 
 #include "svdq_internal.h"
@@ -78,13 +79,29 @@ __device__ inline void lowrank_accumulate(f32x4 (&acc)[TM][TN], const float* __r
   }
 }
 
-// Bias, bf16 rounding and the store of the tile through LDS as 16-byte row
+// GELU in its tanh form (Hendrycks and Gimpel, "Gaussian Error Linear Units",
+// section 2), the activation between a DiT MLP's up and down projections:
+//   gelu(v) = 0.5 v (1 + tanh(u)),  u = sqrt(2/pi) (v + 0.044715 v^3).
+// Since 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)), it is evaluated as
+// v / (1 + 2^z) with z = -2 u log2(e): one exp2 and one reciprocal on the
+// transcendental unit.  Large negative v gives 2^z = inf and -0; large
+// positive v gives v.
+__device__ inline float gelu_tanh(float v) {
+  constexpr float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float c1 = c0 * 0.044715f;
+  const float z = v * __builtin_fmaf(v * v, c1, c0);
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
+// Bias, the activation (act == kActGeluTanh: gelu_tanh of the float32 sum),
+// bf16 rounding and the store of the tile through LDS as 16-byte row
 // segments.  lds must hold BM * BN * 2 bytes; the caller has synchronized the
 // block so that the space is free.
 template <int TM, int TN, int BM, int BN, int THREADS>
 __device__ inline void bias_store(f32x4 (&acc)[TM][TN], const uint16_t* __restrict__ bias,
                                   uint16_t* __restrict__ Y, int ldy, int m0, int n0, int row1,
-                                  int col1, int wr, int wc, int lane, int tid, uint8_t* lds) {
+                                  int col1, int wr, int wc, int lane, int tid, uint8_t* lds,
+                                  int act) {
   const int fr = lane & 15;
   const int fk = lane >> 4;
 
@@ -102,8 +119,9 @@ __device__ inline void bias_store(f32x4 (&acc)[TM][TN], const uint16_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wr + 16 * tm + 4 * fk + i;
-        otile[row * BN + (col ^ (16 * ((row >> 2) & 3)))] =
-            __builtin_bit_cast(uint16_t, (__bf16)(acc[tm][tn][i] + bv));
+        float v = acc[tm][tn][i] + bv;
+        if (act == kActGeluTanh) v = gelu_tanh(v);
+        otile[row * BN + (col ^ (16 * ((row >> 2) & 3)))] = __builtin_bit_cast(uint16_t, (__bf16)v);
       }
   }
   __syncthreads();
@@ -131,11 +149,11 @@ __device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __r
                                           const uint16_t* __restrict__ bias,
                                           uint16_t* __restrict__ Y, int ldy, int m0, int n0,
                                           int row1, int col1, int wr, int wc, int lane, int tid,
-                                          uint8_t* lds) {
+                                          uint8_t* lds, int act) {
   lowrank_accumulate<TM, TN>(acc, T, t_slices, t_stride, r, L2, m0, n0, row1, col1, wr, wc, lane,
                              1.0f);
   bias_store<TM, TN, BM, BN, THREADS>(acc, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
-                                      lds);
+                                      lds, act);
 }
 
 }  // namespace tail

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     const uint8_t* __restrict__ qx, const uint8_t* __restrict__ sx, const float* __restrict__ T,
     int t_slices, long t_stride, int M, int K, int N, int r, const uint16_t* __restrict__ L2,
     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ sw,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   }
 
   tail::bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(acc, bias, Y, N, m0, n0, M, N, wr, wc,
-                                                           lane, tid, lds);
+                                                           lane, tid, lds, act);
 }
 
 int cu_count_mx() {
@@ -246,7 +246,7 @@ int tiles_of(int rows, int cols) {
 template <class C>
 hipError_t launch(const uint8_t* qx, const uint8_t* sx, const float* T, int t_slices, int M, int K,
                   int N, int r, const uint16_t* L2, const uint8_t* Wq, const uint8_t* sw,
-                  const uint16_t* bias, uint16_t* Y, hipStream_t stream) {
+                  const uint16_t* bias, uint16_t* Y, int act, hipStream_t stream) {
   static bool attr = false;  // benign race: every caller sets the same value
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mxfp4_gemm_kernel<C>),
@@ -255,7 +255,7 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, const float* T, int t_sl
     attr = true;
   }
   hipLaunchKernelGGL(mxfp4_gemm_kernel<C>, dim3(tiles_of<C>(M, N)), dim3(C::THREADS), C::LDS,
-                     stream, qx, sx, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias, Y);
+                     stream, qx, sx, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias, Y, act);
   return hipGetLastError();
 }
 
@@ -264,13 +264,13 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, const float* T, int t_sl
 hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
-                             uint16_t* Y, hipStream_t stream) {
+                             uint16_t* Y, int act, hipStream_t stream) {
   const int cus = cu_count_mx();
   if (tiles_of<MxBig>(M, N) >= cus)
-    return launch<MxBig>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, stream);
+    return launch<MxBig>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
   if (tiles_of<MxMed>(M, N) >= cus)
-    return launch<MxMed>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, stream);
-  return launch<MxSmall>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, stream);
+    return launch<MxMed>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+  return launch<MxSmall>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
 }
 
 }  // namespace svdq

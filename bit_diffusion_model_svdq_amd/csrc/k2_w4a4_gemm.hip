@@ -131,7 +131,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     const float* __restrict__ w_scales, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ Y, int ldy, int row0, int row1, int col0, int col1,
     int32_t* __restrict__ P, int full, int rem, int splits, float* __restrict__ part,
-    int t_slices, long t_stride) {
+    int t_slices, long t_stride, int act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -395,7 +395,8 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
 
   tail::lowrank_bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
-      acc, T, t_slices, t_stride, r, L2, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid, lds);
+      acc, T, t_slices, t_stride, r, L2, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid, lds,
+      act);
 }
 
 int cu_count() {
@@ -478,7 +479,7 @@ template <class C, bool EXPORT>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                        const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                        const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                       int col1, int32_t* P, float* part, hipStream_t stream) {
+                       int col1, int32_t* P, float* part, int act, hipStream_t stream) {
   hipError_t e = set_lds_attr<C, EXPORT, kWhole>();
   if (e != hipSuccess) return e;
   SplitPlan plan;
@@ -487,7 +488,7 @@ hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, EXPORT, kWhole>), dim3(plan.full), dim3(C::THREADS),
                      C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
                      col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
-                     (long)(row1 - row0) * r);
+                     (long)(row1 - row0) * r, act);
   e = hipGetLastError();
   if (EXPORT || e != hipSuccess || plan.rem == 0) return e;
   if ((e = set_lds_attr<C, false, kShares>()) != hipSuccess) return e;
@@ -495,12 +496,12 @@ hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kShares>), dim3(plan.rem * plan.splits),
                      dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
                      ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part,
-                     t_slices, (long)(row1 - row0) * r);
+                     t_slices, (long)(row1 - row0) * r, act);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kFixup>), dim3(plan.rem), dim3(C::THREADS),
                      C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
                      col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
-                     (long)(row1 - row0) * r);
+                     (long)(row1 - row0) * r, act);
   return hipGetLastError();
 }
 
@@ -508,17 +509,17 @@ template <bool EXPORT>
 hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                     const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                     const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                    int col1, int32_t* P, float* part, hipStream_t stream) {
+                    int col1, int32_t* P, float* part, int act, hipStream_t stream) {
   switch (pick_tile(row1 - row0, col1 - col0)) {
     case 2:
       return launch_tile<TileBig, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, part, stream);
+                                          row1, col0, col1, P, part, act, stream);
     case 1:
       return launch_tile<TileMed, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, part, stream);
+                                          row1, col0, col1, P, part, act, stream);
     default:
       return launch_tile<TileSmall, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                            row1, col0, col1, P, part, stream);
+                                            row1, col0, col1, P, part, act, stream);
   }
 }
 
@@ -529,9 +530,9 @@ size_t gemm_split_bytes(int M, int K, int N) { return plan_forward(M, N, K).part
 hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int t_slices,
                             int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
-                            float* part, hipStream_t stream) {
+                            float* part, int act, hipStream_t stream) {
   return dispatch<false>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N,
-                         nullptr, part, stream);
+                         nullptr, part, act, stream);
 }
 
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
@@ -539,7 +540,7 @@ hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, in
   (void)M;
   (void)N;
   return dispatch<true>(qx, nullptr, nullptr, 0, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
-                        m1, n0, n1, P, nullptr, stream);
+                        m1, n0, n1, P, nullptr, kActNone, stream);
 }
 
 }  // namespace svdq

@@ -125,6 +125,84 @@ svdq_status guarded(F&& f) {
   }
 }
 
+svdq_status check_act(int act) {
+  if (act != kActNone && act != kActGeluTanh)
+    return fail(SVDQ_ERR_INVALID_ARG, "activation %d is not one of svdq_activation", act);
+  return SVDQ_OK;
+}
+
+svdq_status forward_gemm(int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                         const float* w_scales, const uint16_t* bias, int act, uint16_t* Y,
+                         const void* workspace, size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_shapes(M, K, N, r, true));
+  SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
+  SVDQ_TRY(check_act(act));
+  SVDQ_TRY(check_ptr(workspace, "workspace", false));
+  const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, N, r);
+  if (workspace_bytes < w.bytes)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+  return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales,
+                                    bias, Y, w.part, act, static_cast<hipStream_t>(stream)),
+                   "w4a4_gemm launch");
+}
+
+svdq_status linear_forward(const uint16_t* X, int M, int K, int N, int r, const float* smooth,
+                           const uint16_t* L1, const uint16_t* L2, const uint8_t* Wq,
+                           const float* w_scales, const uint16_t* bias, int act, uint16_t* Y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  // validate everything before launching anything
+  SVDQ_TRY(check_shapes(M, K, N, r, true));
+  SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+  SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
+  SVDQ_TRY(check_act(act));
+  SVDQ_TRY(check_ptr(workspace, "workspace", false));
+  const Workspace w = carve_workspace(workspace, M, K, N, r);
+  if (workspace_bytes < w.bytes)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, false, s),
+                     "smooth_quant_lora_down launch"));
+  return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales,
+                                    bias, Y, w.part, act, s),
+                   "w4a4_gemm launch");
+}
+
+svdq_status forward_gemm_mx(int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                            const uint8_t* w_e8m0, const uint16_t* bias, int act, uint16_t* Y,
+                            const void* workspace, size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_shapes_mx(M, K, N, r));
+  SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
+  SVDQ_TRY(check_act(act));
+  SVDQ_TRY(check_ptr(workspace, "workspace", false));
+  const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, r);
+  if (workspace_bytes < w.bytes)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
+                                     bias, Y, act, static_cast<hipStream_t>(stream)),
+                   "mxfp4_gemm launch");
+}
+
+svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, const float* smooth,
+                              const uint16_t* L1, const uint16_t* L2, const uint8_t* Wq,
+                              const uint8_t* w_e8m0, const uint16_t* bias, int act, uint16_t* Y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  SVDQ_TRY(check_shapes_mx(M, K, N, r));
+  SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+  SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
+  SVDQ_TRY(check_act(act));
+  SVDQ_TRY(check_ptr(workspace, "workspace", false));
+  const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
+  if (workspace_bytes < w.bytes)
+    return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SVDQ_TRY(hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
+                                                      false, s),
+                     "smooth_quant_lora_down (MXFP4) launch"));
+  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
+                                     bias, Y, act, s),
+                   "mxfp4_gemm launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,15 +233,18 @@ svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, co
                               const float* w_scales, const uint16_t* bias, uint16_t* Y,
                               const void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&]() -> svdq_status {
-    SVDQ_TRY(check_shapes(M, K, N, r, true));
-    SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
-    SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const Workspace w = carve_workspace(const_cast<void*>(workspace), M, K, N, r);
-    if (workspace_bytes < w.bytes)
-      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales,
-                                      bias, Y, w.part, static_cast<hipStream_t>(stream)),
-                     "w4a4_gemm launch");
+    return forward_gemm(M, K, N, r, L2, Wq, w_scales, bias, kActNone, Y, workspace,
+                        workspace_bytes, stream);
+  });
+}
+
+svdq_status svdq_forward_gemm_act(int M, int K, int N, int r, const uint16_t* L2,
+                                  const uint8_t* Wq, const float* w_scales, const uint16_t* bias,
+                                  int activation, uint16_t* Y, const void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    return forward_gemm(M, K, N, r, L2, Wq, w_scales, bias, activation, Y, workspace,
+                        workspace_bytes, stream);
   });
 }
 
@@ -173,21 +254,19 @@ svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
                                 uint16_t* Y, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   return guarded([&]() -> svdq_status {
-    // validate everything before launching anything
-    SVDQ_TRY(check_shapes(M, K, N, r, true));
-    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
-    SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
-    SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const Workspace w = carve_workspace(workspace, M, K, N, r);
-    if (workspace_bytes < w.bytes)
-      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, false, s),
-                       "smooth_quant_lora_down launch"));
-    return hip_check(
-        launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales, bias, Y, w.part,
-                         s),
-        "w4a4_gemm launch");
+    return linear_forward(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, kActNone, Y,
+                          workspace, workspace_bytes, stream);
+  });
+}
+
+svdq_status svdq_linear_forward_act(const uint16_t* X, int M, int K, int N, int r,
+                                    const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                    const uint8_t* Wq, const float* w_scales,
+                                    const uint16_t* bias, int activation, uint16_t* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    return linear_forward(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, activation, Y,
+                          workspace, workspace_bytes, stream);
   });
 }
 
@@ -248,15 +327,19 @@ svdq_status svdq_forward_gemm_mxfp4(int M, int K, int N, int r, const uint16_t* 
                                     const uint16_t* bias, uint16_t* Y, const void* workspace,
                                     size_t workspace_bytes, void* stream) {
   return guarded([&]() -> svdq_status {
-    SVDQ_TRY(check_shapes_mx(M, K, N, r));
-    SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
-    SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, r);
-    if (workspace_bytes < w.bytes)
-      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
-                                       bias, Y, static_cast<hipStream_t>(stream)),
-                     "mxfp4_gemm launch");
+    return forward_gemm_mx(M, K, N, r, L2, Wq, w_e8m0, bias, kActNone, Y, workspace,
+                           workspace_bytes, stream);
+  });
+}
+
+svdq_status svdq_forward_gemm_act_mxfp4(int M, int K, int N, int r, const uint16_t* L2,
+                                        const uint8_t* Wq, const uint8_t* w_e8m0,
+                                        const uint16_t* bias, int activation, uint16_t* Y,
+                                        const void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return guarded([&]() -> svdq_status {
+    return forward_gemm_mx(M, K, N, r, L2, Wq, w_e8m0, bias, activation, Y, workspace,
+                           workspace_bytes, stream);
   });
 }
 
@@ -266,20 +349,20 @@ svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, in
                                       const uint8_t* w_e8m0, const uint16_t* bias, uint16_t* Y,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&]() -> svdq_status {
-    SVDQ_TRY(check_shapes_mx(M, K, N, r));
-    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
-    SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
-    SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
-    if (workspace_bytes < w.bytes)
-      return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    SVDQ_TRY(hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
-                                                        false, s),
-                       "smooth_quant_lora_down (MXFP4) launch"));
-    return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
-                                       bias, Y, s),
-                     "mxfp4_gemm launch");
+    return linear_forward_mx(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, kActNone, Y,
+                             workspace, workspace_bytes, stream);
+  });
+}
+
+svdq_status svdq_linear_forward_act_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                          const float* smooth, const uint16_t* L1,
+                                          const uint16_t* L2, const uint8_t* Wq,
+                                          const uint8_t* w_e8m0, const uint16_t* bias,
+                                          int activation, uint16_t* Y, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> svdq_status {
+    return linear_forward_mx(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, activation, Y,
+                             workspace, workspace_bytes, stream);
   });
 }
 

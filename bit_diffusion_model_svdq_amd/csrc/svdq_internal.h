@@ -59,18 +59,22 @@ hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int
                                             uint8_t* sx_e8m0, float* T, bool one_slice,
                                             hipStream_t stream);
 
-// k2: Y = sum_g sx sw P_g + T L2^T + b, bf16 out.  T holds t_slices partial
-// sums of M x r floats, added in order.
+// Output activations of the GEMM epilogue (the values of svdq_activation).
+constexpr int kActNone = 0;
+constexpr int kActGeluTanh = 1;
+
+// k2: Y = act(sum_g sx sw P_g + T L2^T + b), bf16 out.  T holds t_slices
+// partial sums of M x r floats, added in order.
 hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, int t_slices,
                             int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
-                            float* part, hipStream_t stream);
+                            float* part, int act, hipStream_t stream);
 
-// k2, MXFP4 variant: Y = block-scaled FP4 product + T L2^T + b, bf16 out.
+// k2, MXFP4 variant: Y = act(block-scaled FP4 product + T L2^T + b), bf16 out.
 hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
-                             uint16_t* Y, hipStream_t stream);
+                             uint16_t* Y, int act, hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

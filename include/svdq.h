@@ -140,6 +140,23 @@ svdq_status svdq_linear_forward(const uint16_t* X, int M, int K, int N, int r,
                                 uint16_t* Y, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Output activation of the _act entry points, applied in float32 to each
+ * output (after the bias) before its one rounding to bf16.
+ * SVDQ_ACT_GELU_TANH is GELU in its tanh form (Hendrycks and Gimpel,
+ * "Gaussian Error Linear Units", section 2),
+ *   0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))),
+ * the activation between the up and down projections of a DiT MLP; fusing it
+ * here lets the up projection's output feed the down projection directly. */
+typedef enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 } svdq_activation;
+
+/* svdq_linear_forward with `activation` (an svdq_activation value; any other
+ * value is SVDQ_ERR_INVALID_ARG) applied to Y. */
+svdq_status svdq_linear_forward_act(const uint16_t* X, int M, int K, int N, int r,
+                                    const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                    const uint8_t* Wq, const float* w_scales,
+                                    const uint16_t* bias, int activation, uint16_t* Y,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two halves of svdq_linear_forward, for callers that schedule or time
  * them separately.  Stage 1 writes qx, sx, T into the workspace; stage 2
  * reads them and writes Y.  Same requirements as svdq_linear_forward. */
@@ -149,6 +166,11 @@ svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const 
 svdq_status svdq_forward_gemm(int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                               const float* w_scales, const uint16_t* bias, uint16_t* Y,
                               const void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 2 with an output activation, as svdq_linear_forward_act. */
+svdq_status svdq_forward_gemm_act(int M, int K, int N, int r, const uint16_t* L2,
+                                  const uint8_t* Wq, const float* w_scales, const uint16_t* bias,
+                                  int activation, uint16_t* Y, const void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Stage 1 into caller buffers in the canonical layouts: Q(X diag(s)^-1) as
  * qx [M, K/2] and sx [M, K/64], and T = x_hat L1^T [M, r] in float32
@@ -193,7 +215,15 @@ svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, in
                                       const uint8_t* w_e8m0, const uint16_t* bias, uint16_t* Y,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Its two halves, as svdq_forward_quantize / svdq_forward_gemm. */
+/* The MXFP4 forward with an output activation, as svdq_linear_forward_act. */
+svdq_status svdq_linear_forward_act_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                          const float* smooth, const uint16_t* L1,
+                                          const uint16_t* L2, const uint8_t* Wq,
+                                          const uint8_t* w_e8m0, const uint16_t* bias,
+                                          int activation, uint16_t* Y, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* Its two halves, as svdq_forward_quantize / svdq_forward_gemm(_act). */
 svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
                                         const float* smooth, const uint16_t* L1, void* workspace,
                                         size_t workspace_bytes, void* stream);
@@ -201,6 +231,11 @@ svdq_status svdq_forward_gemm_mxfp4(int M, int K, int N, int r, const uint16_t* 
                                     const uint8_t* Wq, const uint8_t* w_e8m0,
                                     const uint16_t* bias, uint16_t* Y, const void* workspace,
                                     size_t workspace_bytes, void* stream);
+svdq_status svdq_forward_gemm_act_mxfp4(int M, int K, int N, int r, const uint16_t* L2,
+                                        const uint8_t* Wq, const uint8_t* w_e8m0,
+                                        const uint16_t* bias, int activation, uint16_t* Y,
+                                        const void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /* Stage 1 into canonical buffers: qx [M, K/2], sx_e8m0 [M, K/32], T [M, r]. */
 svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, const float* smooth,

@@ -67,13 +67,17 @@ WORKLOADS = {
     "mlp_up": Workload("mlp_up", 2, 4608, 3072, 12288, 32, 15, 30.0, 100.0, _lin(5, 1, 16), 1024),
     "mlp_down": Workload("mlp_down", 2, 4608, 12288, 3072, 32, 61, 30.0, 100.0, _lin(5, 1, 16), 1024,
                          act="gelu"),
+    # DiT block at width 3072, 4608 tokens: fused QKV projection and the
+    # attention output projection (the MLP pair above completes the block).
+    "dit_qkv": Workload("dit_qkv", 4, 4608, 3072, 9216, 32, 15, 30.0, 100.0, _lin(5, 1, 16), 1024),
+    "dit_out": Workload("dit_out", 4, 4608, 3072, 3072, 32, 15, 30.0, 100.0, _lin(5, 1, 16), 1024),
     # Small-K, memory-bound UNet widths.
     "smallk_640": Workload("smallk_640", 3, 4096, 640, 640, 32, 3, 30.0, 100.0, _lin(5, 1, 16), 1024),
     "smallk_1280": Workload("smallk_1280", 3, 1024, 1280, 1280, 32, 6, 30.0, 100.0, _lin(5, 1, 16), 1024),
 }
 
 # distinct seed offsets for workloads that share a seed_index
-_SUB = {"mlp_down": 50, "smallk_1280": 50}
+_SUB = {"mlp_down": 50, "smallk_1280": 50, "dit_out": 50}
 
 
 def _rng(w: Workload, tid: int) -> np.random.Generator:
