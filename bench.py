@@ -9,8 +9,15 @@ serve a step from the previous one.
 
 Prints one JSON line (rank 0).  Default workload: the DiT attention
 projection, M=4096 tokens, K=N=3072, rank 32.  Other workloads (--workload)
-are the small-K UNet widths and the DiT MLP linears; --graph replays whole
-rotations of steps from a HIP graph (for the launch-bound small shapes).
+are the small-K UNet widths and the DiT MLP linears.
+
+Timing.  W eager warm-up steps, then K eager steps with HIP events around
+every launch (per-kernel durations as the stream sees them, dispatch gaps
+included).  Then, unless --no-graph, the same K steps are captured into one
+HIP graph and replayed once, untimed, and once timed: `value` and
+`ms_per_step` come from that replay (the launch path a serving loop would
+use).  Per-kernel durations for the roofline come from graphs of K
+back-to-back launches of that kernel alone over the same rotating buffers.
 --workload dit_block times the four SVDQuant linears of a DiT block at width
 3072 and 4608 tokens (fused QKV 3072 -> 9216, attention output 3072 -> 3072,
 MLP up 3072 -> 12288 with GELU fused into its epilogue, MLP down
@@ -51,8 +58,8 @@ def parse():
     ap.add_argument("--format", choices=["int4", "mxfp4"], default="int4",
                     help="int4: symmetric int4, one fp32 scale per 64 channels (int8 MFMA); "
                          "mxfp4: E2M1 with an E8M0 scale per 32 (block-scaled FP4 MFMA)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the steps replayed from a HIP graph; value is then the graph rate")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="report the eager launch loop instead of the HIP graph replay")
     return ap.parse_args()
 
 
@@ -172,38 +179,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    k1_ms = eager_k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    k2_ms = eager_k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_step = total_ms / args.steps
     eager_ms_step = ms_step
 
     graph_info = None
-    if args.graph:
-        # one graph = one full rotation of steps; replayed back to back
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for d in sets:
-                step(d)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for d in sets:
-                step(d)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        replays = max(1, args.steps // nsets)
-        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gs.record()
-        for _ in range(replays):
-            g.replay()
-        ge.record()
-        torch.cuda.synchronize()
-        ms_step = gs.elapsed_time(ge) / (replays * nsets)
-        graph_info = {"replays": replays, "steps_per_graph": nsets, "ms_per_step": round(ms_step, 5),
-                      "eager_ms_per_step": round(eager_ms_step, 5)}
+    if not args.no_graph:
+        def k1_only(i):
+            d = sets[i % nsets]
+            quantize(d["X"], d["s"], d["L1"], d["work"])
+
+        def k2_only(i):
+            d = sets[i % nsets]
+            gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+
+        ms_step = time_graph(torch, lambda i: step(sets[i % nsets]), args.steps)
+        k1_ms = time_graph(torch, k1_only, args.steps)
+        k2_ms = time_graph(torch, k2_only, args.steps)
+        graph_info = {"steps_per_graph": args.steps, "ms_per_step": round(ms_step, 5),
+                      "eager_ms_per_step": round(eager_ms_step, 5),
+                      "eager_k1_us": round(eager_k1_ms * 1e3, 3), "eager_k2_us": round(eager_k2_ms * 1e3, 3)}
 
     ops_main = 2.0 * M * N * K                 # the 4-bit product (int8 or FP4 MFMA)
     ops_low = 2.0 * M * r * (K + N)            # bf16 low-rank branch
@@ -246,7 +242,7 @@ def main():
                   if mx else "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output"),
         "data": "synthetic",
         "config": {"workload": args.workload, "format": args.format, "M": M, "K": K, "N": N, "rank": r,
-                   "group": 32 if mx else 64, "rotated_sets": nsets, "hip_graph": bool(args.graph)},
+                   "group": 32 if mx else 64, "rotated_sets": nsets, "hip_graph": not args.no_graph},
         "tokens_per_s": round(tokens_s, 1),
         "pct_mfma_peak": round(100.0 * tops / peak_mfma, 2),
         "roofline": {
@@ -279,6 +275,32 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds, mx)
     print(json.dumps(out), flush=True)
+
+
+def time_graph(torch, launch, n):
+    """Capture launch(0..n-1) into one HIP graph, replay it once untimed, then once
+    between HIP events on the current stream; returns ms per launch(i)."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):       # warm the launch path outside the capture
+        launch(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gs.record()
+    g.replay()
+    ge.record()
+    torch.cuda.synchronize()
+    ms = gs.elapsed_time(ge) / n
+    del g
+    return ms
 
 
 # The DiT block: (name, workload, activation, input); "H" is the up projection's output.
@@ -364,8 +386,10 @@ def bench_block(args, S, synth, torch):
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = eager_ms_step = start.elapsed_time(end) / args.steps
     dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs]).mean(axis=0)
+    if not args.no_graph:
+        ms_step = time_graph(torch, lambda i: run(sets[i % nsets]), args.steps)
 
     peak_mfma = PEAK_FP4_TFLOPS if mx else PEAK_INT8_TOPS
     sb_row = lambda K: K // 32 if mx else 4 * (K // 64)
@@ -387,7 +411,16 @@ def bench_block(args, S, synth, torch):
             "k2_pct_mfma_peak": round(100.0 * ops_main / (k2_ms * 1e-3) / 1e12 / peak_mfma, 2)}
     dom = max(kern, key=lambda k: kern[k]["k2_us"])
     dk = kern[dom]
-    achieved = dk["k2_ops"] / (dk["k2_us"] * 1e-6) / 1e12
+    dom_us = dk["k2_us"]
+    if not args.no_graph:    # the dominant GEMM alone, K back-to-back launches from a graph
+        j = [L["name"] for L in layers].index(dom)
+        L = layers[j]
+
+        def k2_only(i):
+            e = sets[i % nsets][j]
+            gemm(L["M"], L["K"], e["L2"], e["Wq"], e["ws"], e["b"], acts[L["act"]], e["Y"], e["work"], L["r"])
+        dom_us = round(time_graph(torch, k2_only, args.steps) * 1e3, 3)
+    achieved = dk["k2_ops"] / (dom_us * 1e-6) / 1e12
     tops = ops_total / (ms_step * 1e-3) / 1e12
     kind = "MXFP4" if mx else "W4A4"
     out = {
@@ -406,14 +439,15 @@ def bench_block(args, S, synth, torch):
                   if mx else "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output"),
         "data": "synthetic",
         "config": {"workload": "dit_block", "format": args.format, "M": M, "layers": [L["name"] for L in layers],
-                   "rank": layers[0]["r"], "rotated_sets": nsets},
+                   "rank": layers[0]["r"], "rotated_sets": nsets, "hip_graph": not args.no_graph},
+        "eager_ms_per_step": round(eager_ms_step, 5),
         "tokens_per_s": round(M / (ms_step * 1e-3), 1),
         "pct_mfma_peak": round(100.0 * tops / peak_mfma, 2),
         "roofline": {"kernel": f"{'mxfp4' if mx else 'w4a4'}_gemm (k2) of the {dom} projection", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                      "frac": round(achieved / peak_mfma, 4),
                      "algorithmic": {"ops": dk["k2_ops"], "bytes": dk["k2_bytes"]}, "traffic": None,
-                     "avg_launch_us": dk["k2_us"]},
+                     "avg_launch_us": dom_us},
         "kernels": kern,
         "wall_s_timed": round(wall, 4),
         "pack_s": round(pack_s, 2),
