@@ -1,8 +1,10 @@
-// Shared tail of the two GEMM kernels (int4 and MXFP4): adds the low-rank
-// branch's up projection T L2^T (Terminology Entry, section 2.3, E4 second
-// term) and the bias to a finished fp32 output tile, optionally applies the
-// MLP activation, rounds to bf16 and stores the tile through LDS as 16-byte
-// row segments.
+// Shared head and tail of the two GEMM kernels (int4 and MXFP4).
+//
+// The bias plus the low-rank branch's up projection T L2^T (Terminology
+// Entry, section 2.3, E4 second term), added to the output accumulators
+// before the main loop (MXFP4, whose loop leaves registers for it) or after
+// it (int4); then the optional MLP activation, bf16 rounding, and the store
+// of the tile through LDS as 16-byte row segments.
 #pragma once
 
 #include "svdq_internal.h"
@@ -19,61 +21,123 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
+__device__ inline float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
 // acc[tm][tn] holds the 16x16 tile (wr + 16 tm, wc + 16 tn) of the block's
 // BM x BN output in the MFMA result layout (lane l: column l % 16, rows
 // 4 (l / 16) + i).  T holds t_slices partial sums of M x r floats, t_stride
 // floats apart, added in slice order.  T (times `scale`, a power of two) is
 // split into a bf16 hi/lo pair and enters bf16 MFMAs whose accumulator input
 // is the tile, so the branch keeps ~16 significant bits of T.
-template <int TM, int TN>
-__device__ inline void lowrank_accumulate(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
-                                          int t_slices, long t_stride, int r,
-                                          const uint16_t* __restrict__ L2, int m0, int n0,
-                                          int row1, int col1, int wr, int wc, int lane,
-                                          float scale) {
+//
+// Adds scale * (b[n] + sum_j T[m,j] L2[n,j]) to acc.  `issue` is called once,
+// after the loads of the first 32 ranks (the first EARLY T slices, L2 and the
+// bias) and before any of them is used: a caller that runs this before its
+// main loop puts the loop's first stage there.  Every load is unconditional:
+// rows and columns past the matrix read a clamped valid address (their
+// outputs are never stored), ranks past r read a valid address and are
+// zeroed by a select, so no load waits behind a branch.
+template <int TM, int TN, int EARLY, class Issue>
+__device__ inline void lowrank_bias_add(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
+                                        int t_slices, long t_stride, int r,
+                                        const uint16_t* __restrict__ L2,
+                                        const uint16_t* __restrict__ bias, int m0, int n0,
+                                        int row1, int col1, int wr, int wc, int lane,
+                                        float scale, Issue&& issue) {
+  static_assert(EARLY == 1 || EARLY == 2, "one or two slices travel with the first loads");
   const int fr = lane & 15;
   const int fk = lane >> 4;
-  for (int j0 = 0; j0 < r; j0 += 32) {
+  const float* trow[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) trow[t] = T + (size_t)min(m0 + wr + 16 * t + fr, row1 - 1) * r;
+  const uint16_t* lrow[TN];
+  int bcol[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    bcol[tn] = min(n0 + wc + 16 * tn + fr, col1 - 1);
+    lrow[tn] = L2 + (size_t)bcol[tn] * r;
+  }
+  uint16_t braw[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) braw[tn] = bias ? bias[bcol[tn]] : (uint16_t)0;
+
+  bool issued = false;
+  for (int j0 = 0; j0 < r || !issued; j0 += 32) {
+    const bool step = j0 < r;                  // r = 0: only the bias and `issue`
     const int j = j0 + 8 * fk;
-    const bool j_ok = j < r;
+    const bool j_ok = step && j < r;
+    const int jc = step ? min(j, r - 8) : 0;   // r % 16 == 0, so r - 8 >= 8
+    float4 ta[TM], tb[TM];
+    uint4 lf[TN];
+    if (step) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        ta[t] = *reinterpret_cast<const float4*>(trow[t] + jc);
+        tb[t] = *reinterpret_cast<const float4*>(trow[t] + jc + 4);
+      }
+      float4 ua[TM], ub[TM];
+      if (EARLY == 2) {
+        const long s1 = t_slices > 1 ? t_stride : 0;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          ua[t] = *reinterpret_cast<const float4*>(trow[t] + s1 + jc);
+          ub[t] = *reinterpret_cast<const float4*>(trow[t] + s1 + jc + 4);
+        }
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) lf[tn] = *reinterpret_cast<const uint4*>(lrow[tn] + jc);
+      if (!issued) {
+        issue();
+        issued = true;
+      }
+      if (EARLY == 2 && t_slices > 1)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          ta[t] = add4(ta[t], ua[t]);
+          tb[t] = add4(tb[t], ub[t]);
+        }
+      for (int sl = EARLY; sl < t_slices; ++sl)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          ta[t] = add4(ta[t], *reinterpret_cast<const float4*>(trow[t] + sl * t_stride + jc));
+          tb[t] = add4(tb[t], *reinterpret_cast<const float4*>(trow[t] + sl * t_stride + jc + 4));
+        }
+    } else {
+      issue();
+      issued = true;
+    }
+    if (j0 == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const float bv = __uint_as_float(uint32_t(braw[tn]) << 16) * scale;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tm][tn][i] += bv;
+      }
+    }
+    if (!step) break;
     bf16x8 thi[TM], tlo[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-      const int m = m0 + wr + 16 * t + fr;
-      float tv[8];
-      if (j_ok && m < row1) {
-        const float* tp = T + (size_t)m * r + j;
-        float4 a = *reinterpret_cast<const float4*>(tp);
-        float4 b = *reinterpret_cast<const float4*>(tp + 4);
-        for (int sl = 1; sl < t_slices; ++sl) {
-          const float4 a2 = *reinterpret_cast<const float4*>(tp + sl * t_stride);
-          const float4 b2 = *reinterpret_cast<const float4*>(tp + sl * t_stride + 4);
-          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-          b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
-        }
-        tv[0] = a.x * scale; tv[1] = a.y * scale; tv[2] = a.z * scale; tv[3] = a.w * scale;
-        tv[4] = b.x * scale; tv[5] = b.y * scale; tv[6] = b.z * scale; tv[7] = b.w * scale;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tv[e] = 0.f;
-      }
+      const float tv[8] = {ta[t].x, ta[t].y, ta[t].z, ta[t].w, tb[t].x, tb[t].y, tb[t].z, tb[t].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)tv[e];
+        const float v = j_ok ? tv[e] * scale : 0.f;
+        const __bf16 h = (__bf16)v;
         thi[t][e] = h;
-        tlo[t][e] = (__bf16)(tv[e] - (float)h);
+        tlo[t][e] = (__bf16)(v - (float)h);
       }
     }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-      const int n = n0 + wc + 16 * tn + fr;
-      const bf16x8 lf = (j_ok && n < col1)
-                            ? as_bf16x8(*reinterpret_cast<const uint4*>(L2 + (size_t)n * r + j))
-                            : as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+      const bf16x8 l = as_bf16x8(j_ok ? lf[tn] : make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[tm], lf, acc[tm][tn], 0, 0, 0);
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[tm], lf, acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[tm], l, acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[tm], l, acc[tm][tn], 0, 0, 0);
       }
     }
   }
@@ -93,67 +157,50 @@ __device__ inline float gelu_tanh(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
-// Bias, the activation (act == kActGeluTanh: gelu_tanh of the float32 sum),
-// bf16 rounding and the store of the tile through LDS as 16-byte row
-// segments.  lds must hold BM * BN * 2 bytes; the caller has synchronized the
-// block so that the space is free.
-template <int TM, int TN, int BM, int BN, int THREADS>
-__device__ inline void bias_store(f32x4 (&acc)[TM][TN], const uint16_t* __restrict__ bias,
+// The bias (NULL: none; loads at a clamped column, without branches), the
+// activation (act == kActGeluTanh: gelu_tanh of the float32 sum), bf16
+// rounding and the store of the tile through LDS as 16-byte row segments.
+// row_lds(row) is the LDS address of the tile's row `row` (BN bf16 values);
+// the caller has synchronized the block so that the space is free.
+template <int TM, int TN, int BM, int BN, int THREADS, class RowLds>
+__device__ inline void store_tile(f32x4 (&acc)[TM][TN], const uint16_t* __restrict__ bias,
                                   uint16_t* __restrict__ Y, int ldy, int m0, int n0, int row1,
-                                  int col1, int wr, int wc, int lane, int tid, uint8_t* lds,
+                                  int col1, int wr, int wc, int lane, int tid, RowLds&& row_lds,
                                   int act) {
   const int fr = lane & 15;
   const int fk = lane >> 4;
+  float bv[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    bv[tn] = bias ? __uint_as_float(uint32_t(bias[min(n0 + wc + 16 * tn + fr, col1 - 1)]) << 16)
+                  : 0.f;
 
-  // bias, bf16, then the tile goes through LDS (columns swizzled by 16 elements
-  // per group of 4 rows, so that the 4 row groups of a write hit distinct banks)
-  // and leaves as 16-byte row segments.
-  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  // columns swizzled by 16 elements per group of 4 rows, so that the 4 row
+  // groups of a write hit distinct banks
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int col = wc + 16 * tn + fr;
-    const int n = n0 + col;
-    const float bv = (bias && n < col1) ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int i = 0; i < 4; ++i) {
+      const int row = wr + 16 * tm + 4 * fk + i;
+      uint16_t* orow = row_lds(row);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wr + 16 * tm + 4 * fk + i;
-        float v = acc[tm][tn][i] + bv;
+      for (int tn = 0; tn < TN; ++tn) {
+        const int col = wc + 16 * tn + fr;
+        float v = acc[tm][tn][i] + bv[tn];
         if (act == kActGeluTanh) v = gelu_tanh(v);
-        otile[row * BN + (col ^ (16 * ((row >> 2) & 3)))] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        orow[col ^ (16 * ((row >> 2) & 3))] = __builtin_bit_cast(uint16_t, (__bf16)v);
       }
-  }
+    }
   __syncthreads();
   constexpr int CPR = BN / 8;   // 16-byte chunks per output row
   for (int c = tid; c < BM * CPR; c += THREADS) {
     const int row = c / CPR, ch = c - (c / CPR) * CPR;
     const int m = m0 + row, n = n0 + 8 * ch;
     if (m < row1 && n < col1) {
-      const uint4 v = *reinterpret_cast<const uint4*>(otile + row * BN + 8 * (ch ^ (2 * ((row >> 2) & 3))));
+      const uint4 v = *reinterpret_cast<const uint4*>(row_lds(row) + 8 * (ch ^ (2 * ((row >> 2) & 3))));
       *reinterpret_cast<uint4*>(Y + (size_t)m * ldy + n) = v;
     }
   }
-}
-
-}  // namespace tail
-}  // namespace svdq
-
-namespace svdq {
-namespace tail {
-
-template <int TM, int TN, int BM, int BN, int THREADS>
-__device__ inline void lowrank_bias_store(f32x4 (&acc)[TM][TN], const float* __restrict__ T,
-                                          int t_slices, long t_stride, int r,
-                                          const uint16_t* __restrict__ L2,
-                                          const uint16_t* __restrict__ bias,
-                                          uint16_t* __restrict__ Y, int ldy, int m0, int n0,
-                                          int row1, int col1, int wr, int wc, int lane, int tid,
-                                          uint8_t* lds, int act) {
-  lowrank_accumulate<TM, TN>(acc, T, t_slices, t_stride, r, L2, m0, n0, row1, col1, wr, wc, lane,
-                             1.0f);
-  bias_store<TM, TN, BM, BN, THREADS>(acc, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
-                                      lds, act);
 }
 
 }  // namespace tail

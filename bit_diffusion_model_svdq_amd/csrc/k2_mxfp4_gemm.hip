@@ -29,8 +29,9 @@
 // belongs at its LDS position.
 //
 // The low-rank branch's up projection T L2^T initializes the accumulators
-// before the main loop (its loads travel with the first stage's copies), so
-// that only the bias and the store are left after it.
+// before the main loop (its loads are issued together, without branches, and
+// travel with the first stage's copies), so that only the bias and the store
+// are left after it.
 #include "gemm_tail.h"
 #include "svdq_internal.h"
 
@@ -210,9 +211,8 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     }
   };
 
-  copy_stage(0, 0);
-  tail::lowrank_accumulate<C::TM, C::TN>(acc, T, t_slices, t_stride, r, L2, m0, n0, M, N, wr, wc,
-                                         lane, 1.0f);
+  tail::lowrank_bias_add<C::TM, C::TN, 1>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
+                                          N, wr, wc, lane, 1.0f, [&] { copy_stage(0, 0); });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int s = 0; s < stages; ++s) {
@@ -221,8 +221,10 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     __syncthreads();                 // ... and everyone's; the current buffer is free
   }
 
-  tail::bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(acc, bias, Y, N, m0, n0, M, N, wr, wc,
-                                                           lane, tid, lds, act);
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
+      acc, bias, Y, N, m0, n0, M, N, wr, wc, lane, tid,
+      [&](int row) { return otile + row * C::BN; }, act);
 }
 
 int cu_count_mx() {

@@ -24,10 +24,10 @@
 // and  acc = fma(t, sx, acc).  Two VALU operations per output and group, no
 // integer-to-float conversion.  acc / 256 is taken once at the end.
 //
-// The finished tile is staged through LDS and leaves as 16-byte row segments.
-//
-// Low-rank branch.  acc is the accumulator input of bf16 MFMAs that add
-// T L2^T, with T split into a bf16 hi/lo pair (T keeps ~16 significant bits).
+// Low-rank branch and bias.  The finished tile is scaled by 1/256, the bias
+// is added and then T L2^T by bf16 MFMAs with T split into a bf16 hi/lo pair
+// (T keeps ~16 significant bits); all their loads are issued at once.  The
+// tile is staged through LDS and leaves as 16-byte row segments.
 //
 // Tiling is a template: WM x WN waves, each owning TM x TN tiles of 16x16
 // (tokens x features); two groups per pipeline stage, double-buffered in LDS
@@ -386,17 +386,20 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     }
   }
 
-  // ---- epilogue: 1/256, + L2 T^T (bf16 hi/lo MFMA), + bias, bf16 store
+  // ---- epilogue: 1/256, + b + T L2^T (bf16 hi/lo MFMA), bf16 store
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
+  tail::lowrank_bias_add<C::TM, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1,
+                                          col1, wr, wc, lane, 1.0f, [] {});
 
-  tail::lowrank_bias_store<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
-      acc, T, t_slices, t_stride, r, L2, bias, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid, lds,
-      act);
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
+      acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
+      [&](int row) { return otile + row * C::BN; }, act);
 }
 
 int cu_count() {
