@@ -21,10 +21,11 @@
 // two 16x16x32 bf16 MFMAs, in two 16-byte loads that cover 64 contiguous bytes
 // per row.  The groups of a run go through a window of CH register slots: the
 // loads of group g + CH are issued as soon as group g is processed.  A small
-// window measured faster than a deep one: with every wave of the chip asking
-// for its whole run at once, each wave's first group comes back late.  Loads
-// are branch-free: rows past M and groups past the run re-read valid data
-// that is never used.
+// window measured faster than a deep one: the memory pipeline of a CU takes
+// load instructions only as fast as HBM serves them, so a deep window just
+// stalls each wave at issue, and its groups still arrive at the same pace.
+// Loads are branch-free: rows past M re-read valid data that is never used;
+// the last window refills nothing.
 //
 // Stores.  Codes and scales are collected in LDS and leave at the end as whole
 // row segments of the slice (16-byte stores), so no store shares the in-order
@@ -67,6 +68,7 @@ constexpr int kW = 8;                  // waves per workgroup
 constexpr int kThreads = kW * 64;
 constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
 constexpr size_t kLdsBudget = 152 * 1024;
+constexpr int kMaxSliceGroups = 48;    // the plan below never cuts longer slices
 constexpr int kMaxRT2 = 5;             // two row tiles per block up to r = 80 (register budget)
 
 __device__ inline uint32_t cvt_bf16x2(float a, float b) {  // round-to-nearest-even pair
@@ -160,20 +162,23 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   };
 
   // fl32(1 / s[k]) for the slice, IEEE division, once per workgroup.  The
-  // first kPre values per thread are requested before the first groups, so
-  // that the barrier below does not wait for them; everything up to the
-  // barrier is branch-free (clamped indices, duplicates store equal values).
-  constexpr int kPre = 4;
+  // values are requested before the first groups' loads, and everything up to
+  // the barrier is branch-free (clamped indices, duplicates store equal
+  // values): a branch there would make the compiler wait for every load in
+  // flight.  The planned slices have at most kMaxSliceGroups groups; only a
+  // one-slice launch on a longer row needs the loop, which runs first.
+  constexpr int kPre = kMaxSliceGroups * kGroup / kThreads;
   const int c0 = sg0 * kGroup, nc = (sg1 - sg0) * kGroup;
+  if (nc > kPre * kThreads)
+    for (int k = tid + kPre * kThreads; k < nc; k += kThreads) inv_s[k] = 1.0f / smooth[c0 + k];
   float sv[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) sv[i] = smooth[c0 + min(tid + i * kThreads, nc - 1)];
+  __builtin_amdgcn_sched_barrier(0);   // in-order counter: s must be ahead of the groups
 #pragma unroll
   for (int j = 0; j < CH; ++j) load_group(j, g_begin + j);
 #pragma unroll
   for (int i = 0; i < kPre; ++i) inv_s[min(tid + i * kThreads, nc - 1)] = 1.0f / sv[i];
-  if (nc > kPre * kThreads)
-    for (int k = tid + kPre * kThreads; k < nc; k += kThreads) inv_s[k] = 1.0f / smooth[c0 + k];
 
   f32x4 acc[RTM][RT > 0 ? RT : 1];
 #pragma unroll
@@ -181,7 +186,10 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 #pragma unroll
     for (int j = 0; j < (RT > 0 ? RT : 1); ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // inv_s ready
+  // inv_s ready: the LDS writes are waited for, the group loads stay in flight
+  // (__syncthreads would wait for them too)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
 
   // One group of one row tile from registers: codes, scale, and the lora_down MFMAs.
   auto process = [&](int g, uint4 va, uint4 vb, const uint4* lf, f32x4* at, uint2& codes,
@@ -282,9 +290,11 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   // Whole windows: process a slot, refill it with the group CH ahead, then
   // store.  The refill is unconditional (clamped) so that the loop body has no
   // branch around a load: at a branch join the compiler would have to assume
-  // the worst and wait for every load in flight.
+  // the worst and wait for every load in flight.  The last whole window
+  // refills nothing (its groups past the run would be wasted loads that the
+  // final barrier waits for).
   int gb = g_begin;
-  for (; gb + CH <= g_end; gb += CH) {
+  for (; gb + 2 * CH <= g_end; gb += CH) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       uint2 codes[RTM];
@@ -295,6 +305,21 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       load_group(j, gb + j + CH);
       store_group(gb + j, codes, scales);
     }
+  }
+  // the partial window beyond the next whole one, loaded as the whole one drains
+  const int tail_n = g_end - gb - CH;
+  if (gb + CH <= g_end) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      uint2 codes[RTM];
+      uint32_t scales[RTM];
+#pragma unroll
+      for (int t = 0; t < RTM; ++t)
+        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
+      if (j < tail_n) load_group(j, gb + j + CH);
+      store_group(gb + j, codes, scales);
+    }
+    gb += CH;
   }
   // The last, partial window is already in slots 0 .. g_end - gb - 1.
 #pragma unroll
@@ -423,7 +448,7 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice) {
     if (lds_bytes(p.rtm, G, r) > kLdsBudget) p.rtm = 1;
   } else {
     const int rb = (M + 16 * p.rtm - 1) / (16 * p.rtm);
-    slices = std::max((256 + rb - 1) / rb, (G + 47) / 48);
+    slices = std::max((256 + rb - 1) / rb, (G + kMaxSliceGroups - 1) / kMaxSliceGroups);
     slices = std::max(1, std::min(slices, G / kW));
     while (slices < G && lds_bytes(p.rtm, (G + slices - 1) / slices, r) > kLdsBudget) ++slices;
   }
