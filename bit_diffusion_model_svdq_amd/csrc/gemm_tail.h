@@ -32,10 +32,12 @@ __device__ inline float4 add4(float4 a, float4 b) {
 // split into a bf16 hi/lo pair and enters bf16 MFMAs whose accumulator input
 // is the tile, so the branch keeps ~16 significant bits of T.
 //
-// Adds scale * (b[n] + sum_j T[m,j] L2[n,j]) to acc.  `issue` is called once,
-// after the loads of the first 32 ranks (the first EARLY T slices, L2 and the
-// bias) and before any of them is used: a caller that runs this before its
-// main loop puts the loop's first stage there.  Every load is unconditional:
+// Adds scale * (b[n] + sum_j T[m,j] L2[n,j]) to acc.  `issue` is called once:
+// first of all (EARLY = 0), or after the loads of the first 32 ranks (the
+// first EARLY T slices, L2 and the bias) and before any of them is used.  A
+// caller that runs this before its main loop puts the loop's first stage
+// there; EARLY = 0 keeps the fewest registers live while it issues, the
+// others let the branch's loads travel ahead of it.  Every load is unconditional:
 // rows and columns past the matrix read a clamped valid address (their
 // outputs are never stored), ranks past r read a valid address and are
 // zeroed by a select, so no load waits behind a branch.
@@ -46,7 +48,8 @@ __device__ inline void lowrank_bias_add(f32x4 (&acc)[TM][TN], const float* __res
                                         const uint16_t* __restrict__ bias, int m0, int n0,
                                         int row1, int col1, int wr, int wc, int lane,
                                         float scale, Issue&& issue) {
-  static_assert(EARLY == 1 || EARLY == 2, "one or two slices travel with the first loads");
+  static_assert(EARLY >= 0 && EARLY <= 2, "none, one or two slices ahead of the caller's loads");
+  if (EARLY == 0) issue();   // the caller's loads first: fewer registers live while they issue
   const int fr = lane & 15;
   const int fk = lane >> 4;
   const float* trow[TM];
@@ -63,7 +66,7 @@ __device__ inline void lowrank_bias_add(f32x4 (&acc)[TM][TN], const float* __res
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) braw[tn] = bias ? bias[bcol[tn]] : (uint16_t)0;
 
-  bool issued = false;
+  bool issued = EARLY == 0;
   for (int j0 = 0; j0 < r || !issued; j0 += 32) {
     const bool step = j0 < r;                  // r = 0: only the bias and `issue`
     const int j = j0 + 8 * fk;
@@ -78,7 +81,7 @@ __device__ inline void lowrank_bias_add(f32x4 (&acc)[TM][TN], const float* __res
         tb[t] = *reinterpret_cast<const float4*>(trow[t] + jc + 4);
       }
       float4 ua[TM], ub[TM];
-      if (EARLY == 2) {
+      if (EARLY != 1) {
         const long s1 = t_slices > 1 ? t_stride : 0;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
@@ -92,13 +95,13 @@ __device__ inline void lowrank_bias_add(f32x4 (&acc)[TM][TN], const float* __res
         issue();
         issued = true;
       }
-      if (EARLY == 2 && t_slices > 1)
+      if (EARLY != 1 && t_slices > 1)
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
           ta[t] = add4(ta[t], ua[t]);
           tb[t] = add4(tb[t], ub[t]);
         }
-      for (int sl = EARLY; sl < t_slices; ++sl)
+      for (int sl = EARLY == 1 ? 1 : 2; sl < t_slices; ++sl)
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
           ta[t] = add4(ta[t], *reinterpret_cast<const float4*>(trow[t] + sl * t_stride + jc));

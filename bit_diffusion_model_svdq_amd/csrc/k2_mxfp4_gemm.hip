@@ -29,9 +29,9 @@
 // belongs at its LDS position.
 //
 // The low-rank branch's up projection T L2^T initializes the accumulators
-// before the main loop (its loads are issued together, without branches, and
-// travel with the first stage's copies), so that only the bias and the store
-// are left after it.
+// before the main loop (its loads are issued together, without branches, right
+// after the first stage's copies), so that only the bias and the store are
+// left after it.
 #include "gemm_tail.h"
 #include "svdq_internal.h"
 
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     }
   };
 
-  tail::lowrank_bias_add<C::TM, C::TN, 1>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
+  tail::lowrank_bias_add<C::TM, C::TN, 0>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
                                           N, wr, wc, lane, 1.0f, [&] { copy_stage(0, 0); });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
