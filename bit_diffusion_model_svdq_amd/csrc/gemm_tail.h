@@ -14,6 +14,7 @@ namespace tail {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -163,6 +164,8 @@ __device__ inline float gelu_tanh(float v) {
 // The bias (NULL: none; loads at a clamped column, without branches), the
 // activation (act == kActGeluTanh: gelu_tanh of the float32 sum), bf16
 // rounding and the store of the tile through LDS as 16-byte row segments.
+// The stores are non-temporal: Y streams out to HBM (measured 14 % faster for
+// a plain 25 MB write than stores that allocate in the caches).
 // row_lds(row) is the LDS address of the tile's row `row` (BN bf16 values);
 // the caller has synchronized the block so that the space is free.
 template <int TM, int TN, int BM, int BN, int THREADS, class RowLds>
@@ -200,8 +203,8 @@ __device__ inline void store_tile(f32x4 (&acc)[TM][TN], const uint16_t* __restri
     const int row = c / CPR, ch = c - (c / CPR) * CPR;
     const int m = m0 + row, n = n0 + 8 * ch;
     if (m < row1 && n < col1) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row_lds(row) + 8 * (ch ^ (2 * ((row >> 2) & 3))));
-      *reinterpret_cast<uint4*>(Y + (size_t)m * ldy + n) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row_lds(row) + 8 * (ch ^ (2 * ((row >> 2) & 3))));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Y + (size_t)m * ldy + n));
     }
   }
 }
