@@ -365,6 +365,94 @@ def test_quantizer_matches_exact_rational_evaluation():
     np.testing.assert_array_equal(q[0], np.array(want, np.int8))
 
 
+def _rn32(fr):
+    """Round a Fraction to the nearest float32, ties to even (one IEEE rounding)."""
+    f = F32(float(fr))
+    lo, hi = sorted([f, np.nextafter(f, F32(np.inf) if Fraction(float(f)) < fr else F32(-np.inf))])
+    dlo, dhi = abs(Fraction(float(lo)) - fr), abs(Fraction(float(hi)) - fr)
+    if dlo != dhi:
+        return lo if dlo < dhi else hi
+    return lo if (_bits(lo) & 1) == 0 else hi
+
+
+def _q_exact(vals, weight):
+    """Q of one 64-group with exact rationals: scale fl32(a/7) (weights: two low
+    significand bits cleared), inv fl32(7/a), q = clamp(rne(fl32(v inv)), -7, 7)."""
+    a = max(abs(v) for v in vals)
+    if a == 0:
+        return [0] * len(vals), Fraction(0)
+    scale = _rn32(a / 7)
+    if weight:
+        scale = (np.asarray([scale], F32).view(np.uint32) & np.uint32(0xFFFFFFFC)).view(F32)[0]
+    inv = Fraction(float(_rn32(7 / a)))
+    q = []
+    for v in vals:
+        t = Fraction(float(_rn32(v * inv)))
+        fl = math.floor(t)
+        d = t - fl
+        qi = fl + (1 if d > Fraction(1, 2) or (d == Fraction(1, 2) and fl % 2 == 1) else 0)
+        q.append(max(-7, min(7, qi)))
+    return q, Fraction(float(scale))
+
+
+@pytest.mark.parametrize("K,r", [(64, 0), (64, 1), (128, 0), (128, 1)])
+def test_forward_matches_exact_rationals(K, r):
+    """Brute force with Fractions on tiny layers ([Term] 2.3, E1 and E4): smoothing,
+    the residual R = W diag(s) - L2 L1, both quantizations, the exact group products,
+    the low-rank branch and the bias, each rounding point taken once as the contract
+    fixes it.  Dyadic X, W, L1, L2, b and power-of-two s keep the smoothing exact, so
+    the oracle's codes, scales and P must match exactly and its float64 Y to 1e-15."""
+    g = np.random.default_rng(100 + K + r)
+    M, N = 2, 2
+    X = synth.f32_to_bf16_bits((g.integers(-64, 64, (M, K)) / 16.0).astype(F32))
+    s = np.ldexp(np.ones(K, F32), g.integers(-2, 3, K)).astype(F32)
+    W = (g.integers(-64, 64, (N, K)) / 32.0).astype(F32)
+    L1 = synth.f32_to_bf16_bits((g.integers(-8, 8, (r, K)) / 8.0).astype(F32))
+    L2 = synth.f32_to_bf16_bits((g.integers(-8, 8, (N, r)) / 4.0).astype(F32))
+    b = synth.f32_to_bf16_bits((g.integers(-8, 8, N) / 8.0).astype(F32))
+
+    xv = [[Fraction(float(v)) for v in row] for row in O.bf16_to_f64(X)]
+    sv = [Fraction(float(v)) for v in s]
+    l1 = [[Fraction(float(v)) for v in row] for row in O.bf16_to_f64(L1)]
+    l2 = [[Fraction(float(v)) for v in row] for row in O.bf16_to_f64(L2)]
+    xh = [[x * Fraction(float(_rn32(1 / sk))) for x, sk in zip(row, sv)] for row in xv]
+    R = [[Fraction(float(_rn32(Fraction(float(W[n, k])) * sv[k] - sum(l2[n][j] * l1[j][k] for j in range(r)))))
+          for k in range(K)] for n in range(N)]
+    G = K // 64
+    qx, sx = [[None] * G for _ in range(M)], [[None] * G for _ in range(M)]
+    qw, sw = [[None] * G for _ in range(N)], [[None] * G for _ in range(N)]
+    for gi in range(G):
+        sl = slice(64 * gi, 64 * gi + 64)
+        for m in range(M):
+            qx[m][gi], sx[m][gi] = _q_exact(xh[m][sl], weight=False)
+        for n in range(N):
+            qw[n][gi], sw[n][gi] = _q_exact(R[n][sl], weight=True)
+    T = [[sum(xh[m][k] * l1[j][k] for k in range(K)) for j in range(r)] for m in range(M)]
+
+    pk = O.quantize_activations(X, s, L1)
+    codes = O.unpack_nibbles(pk[0])
+    Wq, wsc = O.quantize_residual(W, s, L1, L2)
+    wcodes = O.unpack_nibbles(Wq)
+    P = O.group_partials(pk[0], Wq)
+    Y = O.forward(X, s, L1, L2, Wq, wsc, b)
+    for gi in range(G):
+        for m in range(M):
+            assert list(codes[m, 64 * gi:64 * gi + 64]) == qx[m][gi]
+            assert Fraction(float(pk[1][m, gi])) == sx[m][gi]
+        for n in range(N):
+            assert list(wcodes[n, 64 * gi:64 * gi + 64]) == qw[n][gi]
+            assert Fraction(float(wsc[n, gi])) == sw[n][gi]
+    bv = [Fraction(float(v)) for v in O.bf16_to_f64(b)]
+    for m in range(M):
+        for n in range(N):
+            want = bv[n] + sum(T[m][j] * l2[n][j] for j in range(r))
+            for gi in range(G):
+                p_exact = sum(a * w for a, w in zip(qx[m][gi], qw[n][gi]))
+                assert P[m, n, gi] == p_exact
+                want += sx[m][gi] * sw[n][gi] * p_exact
+            assert abs(Fraction(float(Y[m, n])) - want) <= abs(want) * Fraction(1, 10 ** 15)
+
+
 def test_quantizer_golden_examples():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "quantizer_examples.txt")
