@@ -433,27 +433,52 @@ hipError_t dispatch(const uint16_t* X, int M, int K, int r, const float* smooth,
 
 }  // namespace
 
-// Row tiles per workgroup and K-slices.  Two row tiles halve the L1 traffic
-// (worth it with a low-rank branch and enough rows).  Slices keep >= 256
-// workgroups and at most 48 groups per slice (a 12288-wide K measured 25 %
-// faster in 48-group slices than in 96-group ones: smaller blocks, two per
-// CU, and a shorter last wave), with >= 8 groups (one per wave) per slice,
-// and are added while the slice's LDS does not fit.
+// Row tiles per workgroup (RTM = 1 or 2) and K-slices, from a cost model in
+// rough microseconds, fitted to measured launches on MI355X:
+//   rounds * (5 + 2 * groups_per_wave * w)          waves of workgroups over 256 CUs
+//   + 10 * (256 - workgroups) / 256 when under 256   idle CUs
+//   + 4 per T slice beyond the first                  the GEMM re-reads every slice of
+//                                                    T for each of its output tiles
+// where w = 1 + 0.5 r / (16 RTM) weighs a group's X bytes with the L1
+// fragments it needs (read from L2 once per 16 RTM rows).  A wave waits one
+// memory round trip per group, so fewer groups per wave shorten a workgroup;
+// more workgroups than CUs add a round.  Slices hold at most kMaxSliceGroups
+// groups and must fit the LDS budget.  Ties keep RTM = 2 and fewer slices.
+// The plan depends on the shape only (it sizes the workspace): 256 CUs.
 K1Plan k1_plan(int M, int K, int r, bool one_slice) {
   K1Plan p;
   const int G = K / kGroup;
-  p.rtm = (r > 0 && r <= 16 * kMaxRT2 && M >= 2048) ? 2 : 1;
-  int slices = 1;
   if (one_slice) {
+    p.rtm = (r > 0 && r <= 16 * kMaxRT2 && M >= 2048) ? 2 : 1;
     if (lds_bytes(p.rtm, G, r) > kLdsBudget) p.rtm = 1;
-  } else {
-    const int rb = (M + 16 * p.rtm - 1) / (16 * p.rtm);
-    slices = std::max((256 + rb - 1) / rb, (G + kMaxSliceGroups - 1) / kMaxSliceGroups);
-    slices = std::max(1, std::min(slices, G / kW));
-    while (slices < G && lds_bytes(p.rtm, (G + slices - 1) / slices, r) > kLdsBudget) ++slices;
+    p.gslice = G;
+    p.slices = 1;
+    return p;
   }
-  p.gslice = (G + slices - 1) / slices;
-  p.slices = (G + p.gslice - 1) / p.gslice;
+  constexpr int kCus = 256;
+  double best = 1e300;
+  for (int rtm = 2; rtm >= 1; --rtm) {
+    if (rtm == 2 && r > 16 * kMaxRT2) continue;
+    const int rb = (M + 16 * rtm - 1) / (16 * rtm);
+    const double w = 1.0 + 0.5 * r / (16.0 * rtm);
+    for (int want = 1; want <= G; ++want) {
+      const int gslice = (G + want - 1) / want;
+      const int slices = (G + gslice - 1) / gslice;
+      if (slices != want || gslice > kMaxSliceGroups) continue;
+      if (lds_bytes(rtm, gslice, r) > kLdsBudget) continue;
+      const int per_wave = (gslice + kW - 1) / kW;
+      const long n = (long)rb * slices;
+      const long rounds = (n + kCus - 1) / kCus;
+      const double cost = rounds * (5.0 + 2.0 * per_wave * w) +
+                          (n < kCus ? 10.0 * (kCus - n) / kCus : 0.0) + 4.0 * (slices - 1);
+      if (cost < best - 1e-9) {
+        best = cost;
+        p.rtm = rtm;
+        p.gslice = gslice;
+        p.slices = slices;
+      }
+    }
+  }
   return p;
 }
 

@@ -161,18 +161,20 @@ def test_workspace_bytes():
     """qx + sx + T; plus the GEMM's split partials when its 256 x 192 tiles leave a
     last partial wave (this container has no GPU: the library assumes 256 CUs)."""
     al = lambda x: (x + 255) // 256 * 256
-    # T: the quantize kernel takes 32-row blocks and cuts K into slices of at
-    # most 48 groups, at least 2 here (128 or 144 blocks -> >= 256 workgroups);
-    # one partial T per slice
+    # T: one partial T per K-slice of the quantize kernel's launch plan (a cost
+    # model over 16- or 32-row blocks and slices of at most 48 groups)
     M, K, N, r = 4096, 3072, 3072, 32          # 16 x 16 = 256 tiles: one full wave
     b = S.svdq_forward_workspace_bytes(M, K, N, r)
-    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(2 * M * r * 4)
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(2 * M * r * 4)   # 128 blocks x 2 slices
     M, K, N = 4608, 12288, 3072                # 18 x 16 = 288 tiles: 32 left, each cut 8 ways
     b = S.svdq_forward_workspace_bytes(M, K, N, r)
-    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(4 * M * r * 4) + 32 * 8 * 256 * 192 * 4
-    M, K, N, r = 256, 1024, 1024, 16           # 16-row blocks, 16 groups: 2 slices of 8
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(5 * M * r * 4) + 32 * 8 * 256 * 192 * 4
+    M, K, N, r = 256, 1024, 1024, 16           # 8 blocks of 32 rows, one slice
     b = S.svdq_forward_workspace_bytes(M, K, N, r)
-    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(2 * M * r * 4)
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(M * r * 4)
+    M, K, N, r = 4608, 3072, 9216, 48          # 144 blocks, one slice (a second would cost the GEMM more)
+    b = S.svdq_forward_workspace_bytes(M, K, N, r)
+    assert b == al(M * K // 2) + al(M * K // 64 * 4) + al(M * r * 4)
     assert S.svdq_forward_workspace_bytes(M, 100, N, r) == 0
     assert S.svdq_forward_workspace_bytes(M, K, 40, r) == 0
     assert S.svdq_forward_workspace_bytes(M, K, N, 24) == 0
