@@ -147,6 +147,35 @@ def test_forward_mx_dit_proj_sampled_rows():
         f"oracle {O.rel_fro(Yref, Yx):.4f}")
 
 
+def test_forward_mx_long_token_batch_sampled_rows():
+    """65536 tokens through the DiT projection's MXFP4 layer (16 times the benchmarked
+    batch): codes and scale bytes bit-exact, Y within tolerance, on sampled rows that
+    include both ends."""
+    say("forward mx long batch, 65536 tokens")
+    M = 16 * synth.WORKLOADS["dit_proj"].M
+    p = packed_mx("dit_proj", M=M)
+    K, N, r = p["K"], p["N"], p["r"]
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(M - 16, M),
+                                     synth.rng_for("dit_proj", 41).choice(M, 224, replace=False)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    Xd, sd, L1d = dev(p["X"]), dev(p["s"]), dev(p["L1"])
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    S.svdq_quantize_activations_mxfp4(Xd, sd, L1d, qx, sx, T)
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r), dtype=torch.uint8, device=DEV)
+    S.svdq_linear_forward_mxfp4(Xd, sd, L1d, dev(p["L2"]), dev(p["Wq"]), dev(p["we"]), dev(p["b"]), Y, ws)
+    torch.cuda.synchronize()
+    qx_o, sx_o, T_o = O.quantize_activations_mx(p["X"][rows], p["s"], p["L1"])[:3]
+    np.testing.assert_array_equal(qx[ridx].cpu().numpy(), qx_o)
+    np.testing.assert_array_equal(sx[ridx].cpu().numpy(), sx_o)
+    assert O.rel_fro(T[ridx].cpu().numpy(), T_o) <= T_REL_FRO
+    Yg = O.bf16_to_f64(Y[ridx].cpu().numpy().view(np.uint16))
+    Yref = O.forward_mx(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["we"], p["b"])
+    check_y(Yg, Yref, "mx long batch sampled")
+
+
 @pytest.mark.parametrize("M,K,N,r", [(200, 640, 208, 48), (1, 128, 16, 16), (77, 256, 48, 0),
                                      (250, 384, 144, 128)])
 def test_forward_mx_ragged_shapes(M, K, N, r):

@@ -205,6 +205,38 @@ def test_forward_dit_proj_sampled_rows():
     say(f"dit_proj method error vs X W^T + b: gpu {O.rel_fro(Yg[rows], Yx):.4f} oracle {O.rel_fro(Yref, Yx):.4f}")
 
 
+def test_forward_long_token_batch_sampled_rows():
+    """65536 tokens through the DiT projection's layer, 16 times the benchmarked batch:
+    thousands of quantize workgroups and 4096 GEMM tiles, byte offsets past 2^26 in
+    every buffer.  Codes and scales bit-exact, T and Y within tolerance, on sampled rows
+    that include both ends."""
+    say("forward long batch, 65536 tokens")
+    base = packed("dit_proj")
+    w = synth.WORKLOADS["dit_proj"]
+    M, K, N, r = 16 * w.M, base["K"], base["N"], base["r"]
+    X = synth.activations(w, M)
+    p = dict(base, X=X, M=M)
+    d = to_device(p)
+    g = synth.rng_for("dit_proj", 32)
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(M - 16, M), g.choice(M, 224, replace=False)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    sx = torch.empty((M, K // 64), dtype=torch.float32, device=DEV)
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    S.svdq_quantize_activations(d["X"], d["s"], d["L1"], qx, sx, T)
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, r), dtype=torch.uint8, device=DEV)
+    S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], Y, ws)
+    torch.cuda.synchronize()
+    qx_o, sx_o, T_o, _ = O.quantize_activations(X[rows], p["s"], p["L1"])
+    np.testing.assert_array_equal(qx[ridx].cpu().numpy(), qx_o)
+    np.testing.assert_array_equal(sx[ridx].cpu().numpy().view(np.uint32), sx_o.view(np.uint32))
+    assert O.rel_fro(T[ridx].cpu().numpy(), T_o) <= T_REL_FRO
+    Yg = O.bf16_to_f64(host(Y[ridx], np.uint16))
+    Yref = O.forward(X[rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+    check_y(Yg, Yref, "long batch sampled")
+
+
 @pytest.mark.parametrize("name", ["mlp_up", "mlp_down"])
 def test_mlp_linears_full_launch_sampled_rows(name):
     """The DiT MLP pair's two linears at full size (4608 tokens; 3072 -> 12288 and
