@@ -167,49 +167,37 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 
   // ---- global -> register staging.  Thread t copies 16-byte piece (t % 4) of
   // rows t/4, t/4 + RPP, ...: piece q holds half h = q % 2 of group q / 2.
+  // Every load is unconditional: rows past the matrix re-read its last row,
+  // and the missing second group of an odd last stage re-reads the last group.
+  // None of those values reaches an output that is stored or exported, and a
+  // branch around a load costs exec-mask bookkeeping in every stage.
   constexpr int RPP = C::THREADS / 4;
   constexpr int APASS = (C::BM + RPP - 1) / RPP;
   constexpr int BPASS = (C::BN + RPP - 1) / RPP;
   const int q = tid & 3;
   const int lrow = tid >> 2;
-  const uint8_t* a_src = qx + (size_t)(m0 + lrow) * KB + q * 16;
-  const uint8_t* b_src = Wq + (size_t)(n0 + lrow) * KB + q * 16;
+  const uint8_t* a_src[APASS];
+  const uint8_t* b_src[BPASS];
+#pragma unroll
+  for (int p = 0; p < APASS; ++p)
+    a_src[p] = qx + (size_t)min(m0 + min(lrow + p * RPP, C::BM - 1), row1 - 1) * KB + q * 16;
+#pragma unroll
+  for (int p = 0; p < BPASS; ++p)
+    b_src[p] = Wq + (size_t)min(n0 + min(lrow + p * RPP, C::BN - 1), col1 - 1) * KB + q * 16;
+  // scale row of this thread: tid < BM an activation row, BM <= tid < BM + BN a weight row
+  const float* s_src = tid < C::BM ? sx + (size_t)min(m0 + tid, row1 - 1) * G
+                                   : w_scales + (size_t)min(n0 + min(tid - C::BM, C::BN - 1), col1 - 1) * G;
   uint4 sa[APASS], sb[BPASS];
   float ss[GS];
   auto gload = [&](int s) {
-    const bool g_ok = s * GS + (q >> 1) < G;
+    const int gq = min(s * GS + (q >> 1), G - 1) - (q >> 1);   // stage's first group, clamped for this piece
 #pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int row = lrow + p * RPP;
-      sa[p] = make_uint4(0u, 0u, 0u, 0u);
-      if ((p + 1) * RPP <= C::BM || row < C::BM)
-        if (g_ok && m0 + row < row1)
-          sa[p] = *reinterpret_cast<const uint4*>(a_src + (size_t)p * RPP * KB + s * (GS * 32));
-    }
+    for (int p = 0; p < APASS; ++p) sa[p] = *reinterpret_cast<const uint4*>(a_src[p] + gq * 32);
 #pragma unroll
-    for (int p = 0; p < BPASS; ++p) {
-      const int row = lrow + p * RPP;
-      sb[p] = make_uint4(0u, 0u, 0u, 0u);
-      if ((p + 1) * RPP <= C::BN || row < C::BN)
-        if (g_ok && n0 + row < col1)
-          sb[p] = *reinterpret_cast<const uint4*>(b_src + (size_t)p * RPP * KB + s * (GS * 32));
-    }
-    if (!EXPORT) {
+    for (int p = 0; p < BPASS; ++p) sb[p] = *reinterpret_cast<const uint4*>(b_src[p] + gq * 32);
+    if (!EXPORT && tid < C::BM + C::BN) {
 #pragma unroll
-      for (int j = 0; j < GS; ++j) ss[j] = 0.f;
-      if (tid < C::BM) {
-        const int m = m0 + tid;
-        if (m < row1)
-#pragma unroll
-          for (int j = 0; j < GS; ++j)
-            if (s * GS + j < G) ss[j] = sx[(size_t)m * G + s * GS + j];
-      } else if (tid < C::BM + C::BN) {
-        const int n = n0 + tid - C::BM;
-        if (n < col1)
-#pragma unroll
-          for (int j = 0; j < GS; ++j)
-            if (s * GS + j < G) ss[j] = w_scales[(size_t)n * G + s * GS + j];
-      }
+      for (int j = 0; j < GS; ++j) ss[j] = s_src[min(s * GS + j, G - 1)];
     }
   };
   auto sstore = [&](int buf) {
