@@ -52,9 +52,10 @@ constexpr int ROWB = 64;           // int8 bytes per row and group in LDS
 constexpr int kMagicBits = 0x4B400000;  // 1.5 * 2^23
 constexpr float kMagic = 12582912.0f;
 
-template <int WM_, int WN_, int TM_, int TN_>
+template <int WM_, int WN_, int TM_, int TN_, int PF_ = 1>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int PF = PF_;            // stages staged in registers ahead of the LDS ones
   static constexpr int BM = WM * TM * 16;   // tokens per workgroup
   static constexpr int BN = WN * TN * 16;   // features per workgroup
   static constexpr int THREADS = WM * WN * 64;
@@ -70,7 +71,7 @@ struct Tile {
 
 using TileBig = Tile<4, 2, 4, 6>;    // 256 x 192, 8 waves
 using TileMed = Tile<2, 2, 4, 4>;    // 128 x 128, 4 waves
-using TileSmall = Tile<2, 2, 2, 2>;  //  64 x  64, 4 waves
+using TileSmall = Tile<2, 2, 2, 2, 2>;  //  64 x  64, 4 waves, two stages ahead
 
 // byte offset of 16-byte slot `slot` (0..3) of row `row` within one group's panel
 __device__ inline int swz(int row, int slot) {
@@ -187,9 +188,13 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   // scale row of this thread: tid < BM an activation row, BM <= tid < BM + BN a weight row
   const float* s_src = tid < C::BM ? sx + (size_t)min(m0 + tid, row1 - 1) * G
                                    : w_scales + (size_t)min(n0 + min(tid - C::BM, C::BN - 1), col1 - 1) * G;
-  uint4 sa[APASS], sb[BPASS];
-  float ss[GS];
-  auto gload = [&](int s) {
+  // register slots: stage t waits in slot (t - first stage) % PF
+  uint4 sa_[C::PF][APASS], sb_[C::PF][BPASS];
+  float ss_[C::PF][GS];
+  auto gload = [&](int s, int slot = 0) {
+    uint4 (&sa)[APASS] = sa_[slot];
+    uint4 (&sb)[BPASS] = sb_[slot];
+    float (&ss)[GS] = ss_[slot];
     const int gq = min(s * GS + (q >> 1), G - 1) - (q >> 1);   // stage's first group, clamped for this piece
 #pragma unroll
     for (int p = 0; p < APASS; ++p) sa[p] = *reinterpret_cast<const uint4*>(a_src[p] + gq * 32);
@@ -200,7 +205,10 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       for (int j = 0; j < GS; ++j) ss[j] = s_src[min(s * GS + j, G - 1)];
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int slot = 0) {
+    const uint4 (&sa)[APASS] = sa_[slot];
+    const uint4 (&sb)[BPASS] = sb_[slot];
+    const float (&ss)[GS] = ss_[slot];
     const int g = q >> 1, h = q & 1;
 #pragma unroll
     for (int p = 0; p < APASS; ++p) {
@@ -310,33 +318,71 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     epilogue(dprev, swp, C::TN - 1);
   };
 
-  if (MODE == kWhole) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int s = 0; s < stages; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < stages) gload(s + 1);
-      const int gv = min(GS, G - s * GS);
+  auto compute_stage = [&](int s, int buf) {
+    const int gv = min(GS, G - s * GS);
 #pragma nounroll
-      for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
-      if (s + 1 < stages) sstore(buf ^ 1);
+    for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
+  };
+  // With registers to spare (PF > 1), the forward runs its last stage inside
+  // the low-rank tail, after that tail's loads have been issued.
+  constexpr bool kLastInTail = C::PF > 1 && MODE == kWhole && !EXPORT;
+
+  if constexpr (C::PF == 1) {
+    if (MODE == kWhole) {
+      gload(0);
+      sstore(0);
       __syncthreads();
+
+      for (int s = 0; s < stages; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < stages) gload(s + 1);
+        const int gv = min(GS, G - s * GS);
+#pragma nounroll
+        for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
+        if (s + 1 < stages) sstore(buf ^ 1);
+        __syncthreads();
+      }
+    } else if (MODE == kShares) {
+      gload(s_begin);
+      sstore(0);
+      __syncthreads();
+
+      for (int s = s_begin; s < s_end; ++s) {
+        const int buf = (s - s_begin) & 1;
+        if (s + 1 < s_end) gload(s + 1);
+        const int gv = min(GS, G - s * GS);
+#pragma nounroll
+        for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
+        if (s + 1 < s_end) sstore(buf ^ 1);
+        __syncthreads();
+      }
     }
-  } else if (MODE == kShares) {
-    gload(s_begin);
-    sstore(0);
-    __syncthreads();
-
-    for (int s = s_begin; s < s_end; ++s) {
-      const int buf = (s - s_begin) & 1;
-      if (s + 1 < s_end) gload(s + 1);
-      const int gv = min(GS, G - s * GS);
-#pragma nounroll
-      for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
-      if (s + 1 < s_end) sstore(buf ^ 1);
-      __syncthreads();
+  } else if (MODE != kFixup) {
+    // Stages sb+1 .. sb+PF wait in registers while stage sb is in LDS; after
+    // each stage the next one goes to LDS and its slot takes the stage PF
+    // further.  The barrier waits for the LDS stores only: the loads in
+    // flight stay in flight (__syncthreads would drain them).
+    const int sb = MODE == kShares ? s_begin : 0;
+    const int se = MODE == kShares ? s_end : stages;
+    const int last = kLastInTail ? se - 1 : se;   // stages computed here
+    gload(sb, 0);
+    sstore(0, 0);
+#pragma unroll
+    for (int j = 1; j <= C::PF; ++j)
+      if (sb + j < se) gload(sb + j, j % C::PF);
+    lds_barrier();
+    for (int s0 = sb; s0 < last; s0 += C::PF) {
+#pragma unroll
+      for (int j = 0; j < C::PF; ++j) {
+        const int s = s0 + j;
+        if (s < last) {
+          const int buf = (s - sb) & 1;
+          compute_stage(s, buf);
+          if (s + 1 < se) sstore(buf ^ 1, (j + 1) % C::PF);
+          if (s + 1 + C::PF < se) gload(s + 1 + C::PF, (j + 1) % C::PF);
+          lds_barrier();
+        }
+      }
     }
   }
 
@@ -375,14 +421,28 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   }
 
   // ---- epilogue: 1/256, + b + T L2^T (bf16 hi/lo MFMA), bf16 store
+  if constexpr (kLastInTail) {
+    tail::lowrank_bias_add<C::TM, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1,
+                                            col1, wr, wc, lane, 1.0f, [&] {
+      compute_stage(stages - 1, (stages - 1) & 1);
 #pragma unroll
-  for (int tm = 0; tm < C::TM; ++tm)
+      for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn)
+        for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
-  tail::lowrank_bias_add<C::TM, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1,
-                                          col1, wr, wc, lane, 1.0f, [] {});
+          for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
+    });
+    __syncthreads();   // the last stage's buffer is read before the tile is staged over it
+  } else {
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tm][tn][i] *= (1.0f / 256.0f);
+    tail::lowrank_bias_add<C::TM, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1,
+                                            col1, wr, wc, lane, 1.0f, [] {});
+  }
 
   uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
   tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(

@@ -59,6 +59,17 @@ hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int
                                             uint8_t* sx_e8m0, float* T, bool one_slice,
                                             hipStream_t stream);
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) and leaves its global loads in flight.  __syncthreads also waits
+// for those (vmcnt 0), which costs a pipeline that keeps stages in flight in
+// registers.  The fences, limited to the local address space, stop the
+// compiler from moving LDS accesses across the barrier.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Output activations of the GEMM epilogue (the values of svdq_activation).
 constexpr int kActNone = 0;
 constexpr int kActGeluTanh = 1;
