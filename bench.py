@@ -139,8 +139,9 @@ def main():
                + r * (K + N) * 2 + K * 4 + N * 2)
     nsets = max(2, -(-args.rotate_mb * (1 << 20) // per_set))
     sets = []
+    # the forward reads MXFP4 weight scales k-tiled; the oracle leg keeps them row-major
     base = dict(X=t(X), s=t(pk["smooth"]), L1=t(pk["L1"]), L2=t(pk["L2"]), Wq=t(pk["Wq"]),
-                ws=t(pk["w_scales"]), b=t(b))
+                ws=t(S.svdq_mxfp4_tile_scales(pk["w_scales"]) if mx else pk["w_scales"]), b=t(b))
     for i in range(nsets):
         d = {k: v.clone() for k, v in base.items()}
         d["Y"] = torch.empty((M, N), dtype=torch.int16, device=dev)
@@ -351,8 +352,9 @@ def bench_block(args, S, synth, torch):
     for i in range(nsets):
         d = []
         for L in layers:
+            wsc = L["pk"]["w_scales"]
             e = dict(s=t(L["pk"]["smooth"]), L1=t(L["pk"]["L1"]), L2=t(L["pk"]["L2"]), Wq=t(L["pk"]["Wq"]),
-                     ws=t(L["pk"]["w_scales"]), b=t(L["b"]),
+                     ws=t(S.svdq_mxfp4_tile_scales(wsc) if mx else wsc), b=t(L["b"]),
                      Y=torch.empty((L["M"], L["N"]), dtype=torch.int16, device=dev),
                      work=torch.empty(L["ws_bytes"], dtype=torch.uint8, device=dev))
             e["X"] = t(L["X"]) if L["X"] is not None else None

@@ -46,7 +46,7 @@ EXPORTS = [
     "svdq_quantize_residual_mxfp4", "svdq_forward_workspace_bytes_mxfp4", "svdq_linear_forward_mxfp4",
     "svdq_forward_quantize_mxfp4", "svdq_forward_gemm_mxfp4", "svdq_quantize_activations_mxfp4",
     "svdq_linear_forward_act", "svdq_forward_gemm_act", "svdq_linear_forward_act_mxfp4",
-    "svdq_forward_gemm_act_mxfp4",
+    "svdq_forward_gemm_act_mxfp4", "svdq_mxfp4_tiled_scale_bytes", "svdq_mxfp4_tile_scales",
 ]
 
 # svdq_activation
@@ -89,6 +89,8 @@ _sig = {
     "svdq_forward_gemm_act": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "svdq_linear_forward_act_mxfp4": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
     "svdq_forward_gemm_act_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P],
+    "svdq_mxfp4_tiled_scale_bytes": [_I, _I],
+    "svdq_mxfp4_tile_scales": [_P, _I, _I, _P],
     "svdq_status_string": [_I],
     "svdq_last_error": [],
 }
@@ -98,6 +100,7 @@ for _name, _args in _sig.items():
     _f.restype = _I
 _lib.svdq_forward_workspace_bytes.restype = ctypes.c_size_t
 _lib.svdq_forward_workspace_bytes_mxfp4.restype = ctypes.c_size_t
+_lib.svdq_mxfp4_tiled_scale_bytes.restype = ctypes.c_size_t
 _lib.svdq_status_string.restype = ctypes.c_char_p
 _lib.svdq_last_error.restype = ctypes.c_char_p
 
@@ -276,7 +279,8 @@ def svdq_last_error() -> str:
 
 # ------------------------------------------------------------ MXFP4 variant
 def svdq_quantize_residual_mxfp4(W, smooth, L1, L2):
-    """Wq [N, K/2] (E2M1 codes) and w_e8m0 [N, K/32] from W, s, L1 [r, K], L2 [N, r] (host arrays)."""
+    """Wq [N, K/2] (E2M1 codes) and row-major w_e8m0 [N, K/32] from W, s, L1 [r, K], L2 [N, r]
+    (host arrays).  The forward takes the scales k-tiled (svdq_mxfp4_tile_scales)."""
     W = _host(W, np.float32)
     N, K = W.shape
     s = _host(smooth, np.float32, (K,))
@@ -289,6 +293,20 @@ def svdq_quantize_residual_mxfp4(W, smooth, L1, L2):
                                            _hp(L2) if r else None, r, _hp(Wq), _hp(we))
     _check(st, "svdq_quantize_residual_mxfp4")
     return Wq, we
+
+
+def svdq_mxfp4_tiled_scale_bytes(rows: int, K: int) -> int:
+    return int(_lib.svdq_mxfp4_tiled_scale_bytes(rows, K))
+
+
+def svdq_mxfp4_tile_scales(scales):
+    """Row-major E8M0 scales [rows, K/32] (host) -> the k-tiled layout [ceil(K/256), rows, 8]."""
+    sc = _host(scales, np.uint8)
+    rows, nb = sc.shape
+    K = 32 * nb
+    out = np.empty(((K + 255) // 256, rows, 8), np.uint8)
+    _check(_lib.svdq_mxfp4_tile_scales(_hp(sc), rows, K, _hp(out)), "svdq_mxfp4_tile_scales")
+    return out
 
 
 def svdq_forward_workspace_bytes_mxfp4(M: int, K: int, N: int, r: int) -> int:

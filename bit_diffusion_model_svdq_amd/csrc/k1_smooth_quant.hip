@@ -46,7 +46,10 @@
 // power-of-two scale and rounds to nearest even with saturation, two
 // elements per instruction, keeping the sign of a value that rounds to zero.
 // A block whose scale would be the subnormal 2^-127 (absmax < 2^-125) is
-// converted as v * 2^127 with scale 1 instead.
+// converted as v * 2^127 with scale 1 instead.  The scale bytes leave row-major
+// [M, K/32], or k-tiled for the GEMM: per 256 channels, the 8 bytes of each
+// row, rows consecutive ([K/256][sx_rows][8]), so that the GEMM copies a
+// tile's scales of one stage as one contiguous run.
 //
 // lora_down.  x_hat enters the MFMA as a bf16 hi/lo pair (hi = x_hat with the
 // low 16 bits cleared, lo = bf16(x_hat - hi), an exact difference), so T keeps
@@ -114,7 +117,7 @@ template <int RT, int RTM, bool MX>
 __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
     const uint16_t* __restrict__ L1, int r, uint8_t* __restrict__ qx, void* __restrict__ sx_out,
-    float* __restrict__ T, int gslice) {
+    float* __restrict__ T, int gslice, int sx_rows) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int NL = RT > 0 ? 2 * RT : 1;
   constexpr int CH = window<RT, RTM>();
@@ -188,8 +191,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 
   // inv_s ready: the LDS writes are waited for, the group loads stay in flight
   // (__syncthreads would wait for them too)
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt untouched
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
 
   // One group of one row tile from registers: codes, scale, and the lora_down MFMAs.
   auto process = [&](int g, uint4 va, uint4 vb, const uint4* lf, f32x4* at, uint2& codes,
@@ -350,9 +352,12 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       if (m0 + rr < M) {
         const uint32_t v = lscales[rr * gslice + c];
         if constexpr (MX) {
-          uint8_t* d = static_cast<uint8_t*>(sx_out) + (size_t)(m0 + rr) * 2 * G + 2 * (sg0 + c);
-          d[0] = (uint8_t)(v & 0xFFu);
-          d[1] = (uint8_t)(v >> 8);
+          // the group's two E8M0 bytes: row-major [M, K/32], or k-tiled
+          // [K/256][sx_rows][8] (sx_rows > 0) as the block-scaled GEMM reads them
+          const int g = sg0 + c;
+          const size_t at = sx_rows > 0 ? ((size_t)(g >> 2) * sx_rows + m0 + rr) * 8 + 2 * (g & 3)
+                                        : (size_t)(m0 + rr) * 2 * G + 2 * g;
+          *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(sx_out) + at) = (uint16_t)v;
         } else {
           static_cast<float*>(sx_out)[(size_t)(m0 + rr) * G + sg0 + c] = __uint_as_float(v);
         }
@@ -390,7 +395,8 @@ size_t lds_bytes(int rtm, int gslice, int r) {
 
 template <int RT, int RTM, bool MX>
 hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
-                  const uint16_t* L1, uint8_t* qx, void* sx, float* T, hipStream_t stream) {
+                  const uint16_t* L1, uint8_t* qx, void* sx, float* T, int sx_rows,
+                  hipStream_t stream) {
   const size_t lds = lds_bytes(RTM, p.gslice, r);
   auto kern = smooth_quant_lora_down_kernel<RT, RTM, MX>;
   if (lds > 64 * 1024) {
@@ -400,33 +406,34 @@ hipError_t launch(const K1Plan& p, const uint16_t* X, int M, int K, int r, const
   }
   const int rb = (M + 16 * RTM - 1) / (16 * RTM);
   hipLaunchKernelGGL(kern, dim3(rb, p.slices), dim3(kThreads), lds, stream, X, M, K, smooth, L1,
-                     r, qx, sx, T, p.gslice);
+                     r, qx, sx, T, p.gslice, sx_rows);
   return hipGetLastError();
 }
 
 template <int RT, bool MX>
 hipError_t launch_rt(const K1Plan& p, const uint16_t* X, int M, int K, int r, const float* smooth,
-                     const uint16_t* L1, uint8_t* qx, void* sx, float* T, hipStream_t stream) {
+                     const uint16_t* L1, uint8_t* qx, void* sx, float* T, int sx_rows,
+                     hipStream_t stream) {
   if constexpr (RT <= kMaxRT2)
-    if (p.rtm == 2) return launch<RT, 2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-  return launch<RT, 1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    if (p.rtm == 2) return launch<RT, 2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+  return launch<RT, 1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
 }
 
 template <bool MX>
 hipError_t dispatch(const uint16_t* X, int M, int K, int r, const float* smooth,
                     const uint16_t* L1, uint8_t* qx, void* sx, float* T, bool one_slice,
-                    hipStream_t stream) {
+                    int sx_rows, hipStream_t stream) {
   const K1Plan p = k1_plan(M, K, r, one_slice);
   switch (r / 16) {
-    case 0: return launch_rt<0, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 1: return launch_rt<1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 2: return launch_rt<2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 3: return launch_rt<3, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 4: return launch_rt<4, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 5: return launch_rt<5, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 6: return launch_rt<6, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 7: return launch_rt<7, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
-    case 8: return launch_rt<8, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, stream);
+    case 0: return launch_rt<0, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 1: return launch_rt<1, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 2: return launch_rt<2, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 3: return launch_rt<3, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 4: return launch_rt<4, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 5: return launch_rt<5, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 6: return launch_rt<6, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 7: return launch_rt<7, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
+    case 8: return launch_rt<8, MX>(p, X, M, K, r, smooth, L1, qx, sx, T, sx_rows, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -485,14 +492,14 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice) {
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
                                          float* sx, float* T, bool one_slice, hipStream_t stream) {
-  return dispatch<false>(X, M, K, r, smooth, L1, qx, sx, T, one_slice, stream);
+  return dispatch<false>(X, M, K, r, smooth, L1, qx, sx, T, one_slice, 0, stream);
 }
 
 hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int r,
                                             const float* smooth, const uint16_t* L1, uint8_t* qx,
                                             uint8_t* sx_e8m0, float* T, bool one_slice,
-                                            hipStream_t stream) {
-  return dispatch<true>(X, M, K, r, smooth, L1, qx, sx_e8m0, T, one_slice, stream);
+                                            int sx_rows, hipStream_t stream) {
+  return dispatch<true>(X, M, K, r, smooth, L1, qx, sx_e8m0, T, one_slice, sx_rows, stream);
 }
 
 }  // namespace svdq

@@ -19,7 +19,9 @@
 // Data path: two 128-channel steps per pipeline stage; the stage's A and B
 // rows (128 bytes each) and scale bytes (8 per row) are copied from global
 // memory straight into LDS (global_load_lds: no registers, no ALU), double
-// buffered.  The compiler makes every LDS read wait for all copies in flight
+// buffered.  Both scale operands come k-tiled ([ceil(K/256)][rows][8]): a
+// tile's scales of one stage are then one contiguous run, 1 KB per copy,
+// where row-major [rows, K/32] scales would cost one 8-byte piece per row.  The compiler makes every LDS read wait for all copies in flight
 // (it cannot tell the two buffers apart), so a wave first reads all of its
 // fragments and scales of the stage, then issues its copies of the next stage,
 // then runs the stage's 2 x TM x TN MFMAs while the copies travel.
@@ -57,13 +59,15 @@ struct MxTile {
   static constexpr int THREADS = WAVES * 64;
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int B_BYTES = BN * ROWB;
-  static constexpr int SA_BYTES = BM * SROWB;
-  static constexpr int SB_BYTES = BN * SROWB;
+  // scale bytes of a stage, rounded up to whole 1 KB copies (the rows past
+  // the tile that fill the rest are never read)
+  static constexpr int SA_BYTES = (BM * SROWB + 1023) / 1024 * 1024;
+  static constexpr int SB_BYTES = (BN * SROWB + 1023) / 1024 * 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   static constexpr int OUT = BM * BN * 2;
   static constexpr int LDS = (2 * STAGE > OUT ? 2 * STAGE : OUT);
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB copies");
-  static_assert(SA_BYTES % 256 == 0 && SB_BYTES % 256 == 0, "whole 256 B copies");
+  static_assert(SA_BYTES % 1024 == 0 && SB_BYTES % 1024 == 0, "whole 1 KB copies");
 };
 
 using MxBig = MxTile<4, 2, 4, 6>;    // 256 x 192, 8 waves
@@ -95,8 +99,9 @@ __device__ inline int swz(int row, int c) { return row * ROWB + ((c ^ swz_key(ro
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
-    const uint8_t* __restrict__ qx, const uint8_t* __restrict__ sx, const float* __restrict__ T,
-    int t_slices, long t_stride, int M, int K, int N, int r, const uint16_t* __restrict__ L2,
+    const uint8_t* __restrict__ qx, const uint8_t* __restrict__ sx, int sx_rows,
+    const float* __restrict__ T, int t_slices, long t_stride, int M, int K, int N, int r,
+    const uint16_t* __restrict__ L2,
     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ sw,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -104,7 +109,6 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int KB = K / 2;            // packed bytes per row
-  const int SB = K / 32;           // scale bytes per row
   const int ksteps = K / KS;
   const int stages = (ksteps + SK - 1) / SK;
   const int ntm = (M + C::BM - 1) / C::BM;
@@ -135,20 +139,24 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
       __builtin_amdgcn_global_load_lds(g, (lds_ptr)(dst + q * 1024), 16, 0, 0);
     }
   };
-  auto copy_scales = [&](const uint8_t* src, int nrows_total, int row_base, int s, uint8_t* dst,
+  // Scales are k-tiled: stage s of rows [0, rows) is one run of 8 * rows
+  // bytes (rows even), so a tile's scales of a stage are contiguous and move
+  // as 1 KB copies of 16 bytes per lane.  Lanes past the run re-read its last
+  // 16 bytes, into LDS rows that are never read.  An odd last stage has no
+  // second step; its upper 4 bytes per row are never used.
+  auto copy_scales = [&](const uint8_t* src, int rows, int row_base, int s, uint8_t* dst,
                          int bytes) {
-    const int jrow = lane >> 1, half = lane & 1;
-    for (int q = wave; q < bytes / 256; q += C::WAVES) {
-      const int row = q * 32 + jrow;
-      const int h = (s * SK + half >= ksteps) ? 0 : half;
-      const uint8_t* g = src + (size_t)min(row_base + row, nrows_total - 1) * SB + s * SROWB + h * 4;
-      __builtin_amdgcn_global_load_lds(g, (lds_ptr)(dst + q * 256), 4, 0, 0);
+    const uint8_t* run = src + (size_t)s * rows * SROWB;
+    const int last = rows * SROWB - 16;
+    for (int q = wave; q < bytes / 1024; q += C::WAVES) {
+      const int off = min(row_base * SROWB + q * 1024 + lane * 16, last);
+      __builtin_amdgcn_global_load_lds(run + off, (lds_ptr)(dst + q * 1024), 16, 0, 0);
     }
   };
   auto copy_stage = [&](int s, int buf) {
     copy_rows(qx, M, m0, KB, s, stage_a(buf), C::A_BYTES);
     copy_rows(Wq, N, n0, KB, s, stage_b(buf), C::B_BYTES);
-    copy_scales(sx, M, m0, s, stage_sa(buf), C::SA_BYTES);
+    copy_scales(sx, sx_rows, m0, s, stage_sa(buf), C::SA_BYTES);
     copy_scales(sw, N, n0, s, stage_sb(buf), C::SB_BYTES);
   };
 
@@ -246,9 +254,10 @@ int tiles_of(int rows, int cols) {
 }
 
 template <class C>
-hipError_t launch(const uint8_t* qx, const uint8_t* sx, const float* T, int t_slices, int M, int K,
-                  int N, int r, const uint16_t* L2, const uint8_t* Wq, const uint8_t* sw,
-                  const uint16_t* bias, uint16_t* Y, int act, hipStream_t stream) {
+hipError_t launch(const uint8_t* qx, const uint8_t* sx, int sx_rows, const float* T, int t_slices,
+                  int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
+                  const uint8_t* sw, const uint16_t* bias, uint16_t* Y, int act,
+                  hipStream_t stream) {
   static bool attr = false;  // benign race: every caller sets the same value
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mxfp4_gemm_kernel<C>),
@@ -257,22 +266,23 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, const float* T, int t_sl
     attr = true;
   }
   hipLaunchKernelGGL(mxfp4_gemm_kernel<C>, dim3(tiles_of<C>(M, N)), dim3(C::THREADS), C::LDS,
-                     stream, qx, sx, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias, Y, act);
+                     stream, qx, sx, sx_rows, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias,
+                     Y, act);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, const float* T,
+hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_rows, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
                              uint16_t* Y, int act, hipStream_t stream) {
   const int cus = cu_count_mx();
   if (tiles_of<MxBig>(M, N) >= cus)
-    return launch<MxBig>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+    return launch<MxBig>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
   if (tiles_of<MxMed>(M, N) >= cus)
-    return launch<MxMed>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
-  return launch<MxSmall>(qx, sx_e8m0, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+    return launch<MxMed>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+  return launch<MxSmall>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
 }
 
 }  // namespace svdq

@@ -501,6 +501,27 @@ svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const flo
   }
 }
 
+size_t svdq_mxfp4_tiled_scale_bytes(int rows, int K) {
+  if (rows < 1 || K < 128 || K % 128) return 0;
+  return (size_t)((K + 255) / 256) * rows * 8;
+}
+
+svdq_status svdq_mxfp4_tile_scales(const uint8_t* scales, int rows, int K, uint8_t* tiled) {
+  if (!scales || !tiled) return fail(SVDQ_ERR_INVALID_ARG, "NULL scales or tiled");
+  if (rows < 1 || K < 128 || K % 128)
+    return fail(SVDQ_ERR_INVALID_ARG, "rows must be >= 1 and K a positive multiple of 128 (got %d, %d)",
+                rows, K);
+  const int nb = K / 32;                  // scale bytes per row
+  const int nt = (K + 255) / 256;         // 256-channel k-tiles
+  for (int t = 0; t < nt; ++t)
+    for (int n = 0; n < rows; ++n)
+      for (int j = 0; j < 8; ++j) {
+        const int b = 8 * t + j;
+        tiled[((size_t)t * rows + n) * 8 + j] = b < nb ? scales[(size_t)n * nb + b] : (uint8_t)127;
+      }
+  return SVDQ_OK;
+}
+
 svdq_status svdq_pack_weights(const float* W, int N, int K, const float* act_absmax,
                               const svdq_pack_params* p, float* smooth, uint16_t* L1,
                               uint16_t* L2, uint8_t* Wq, float* w_scales, double* sigma) {

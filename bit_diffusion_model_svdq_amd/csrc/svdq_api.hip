@@ -40,12 +40,14 @@ Workspace carve_workspace(void* base, int M, int K, int N, int r) {
   return w;
 }
 
-// MXFP4 workspace: qx [M, K/2] | sx [M, K/32] E8M0 bytes | T [slices, M, r].
+// MXFP4 workspace: qx [M, K/2] | sx k-tiled E8M0 bytes [ceil(K/256)][sx_rows][8]
+// | T [slices, M, r].
 MxWorkspace carve_workspace_mx(void* base, int M, int K, int r) {
   MxWorkspace w;
   uint8_t* p = static_cast<uint8_t*>(base);
+  w.sx_rows = (M + 1) & ~1;
   const size_t qx_bytes = align256((size_t)M * (K / 2));
-  const size_t sx_bytes = align256((size_t)M * (K / 32));
+  const size_t sx_bytes = align256((size_t)((K + 255) / 256) * w.sx_rows * 8);
   w.t_slices = k1_plan(M, K, r, false).slices;
   const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
   w.qx = p;
@@ -177,8 +179,8 @@ svdq_status forward_gemm_mx(int M, int K, int N, int r, const uint16_t* L2, cons
   const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, r);
   if (workspace_bytes < w.bytes)
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
-  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
-                                     bias, Y, act, static_cast<hipStream_t>(stream)),
+  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.sx_rows, w.T, w.t_slices, M, K, N, r, L2, Wq,
+                                     w_e8m0, bias, Y, act, static_cast<hipStream_t>(stream)),
                    "mxfp4_gemm launch");
 }
 
@@ -196,10 +198,10 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   SVDQ_TRY(hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
-                                                      false, s),
+                                                      false, w.sx_rows, s),
                      "smooth_quant_lora_down (MXFP4) launch"));
-  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_e8m0,
-                                     bias, Y, act, s),
+  return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.sx_rows, w.T, w.t_slices, M, K, N, r, L2, Wq,
+                                     w_e8m0, bias, Y, act, s),
                    "mxfp4_gemm launch");
 }
 
@@ -317,7 +319,8 @@ svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
-                                                      false, static_cast<hipStream_t>(stream)),
+                                                      false, w.sx_rows,
+                                                      static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down (MXFP4) launch");
   });
 }
@@ -376,7 +379,7 @@ svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, con
     SVDQ_TRY(check_ptr(sx_e8m0, "sx_e8m0", false));
     SVDQ_TRY(check_ptr(T, "T", r == 0));
     return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, qx, sx_e8m0, T, true,
-                                                      static_cast<hipStream_t>(stream)),
+                                                      0, static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down (MXFP4) launch");
   });
 }

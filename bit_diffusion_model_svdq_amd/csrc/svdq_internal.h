@@ -28,10 +28,12 @@ struct Workspace {
 };
 Workspace carve_workspace(void* base, int M, int K, int N, int r);
 
-// MXFP4 workspace: qx [M, K/2] | sx [M, K/32] E8M0 bytes | T [slices, M, r].
+// MXFP4 workspace: qx [M, K/2] | sx k-tiled E8M0 bytes [ceil(K/256)][sx_rows][8]
+// | T [slices, M, r].
 struct MxWorkspace {
   uint8_t* qx;
   uint8_t* sx;
+  int sx_rows;      // M rounded up to even: 16-byte runs of two rows stay aligned
   float* T;
   int t_slices;
   size_t bytes;
@@ -53,11 +55,13 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice);
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
                                          float* sx, float* T, bool one_slice, hipStream_t stream);
-// The same with MXFP4 codes: qx [M, K/2] E2M1 patterns, sx_e8m0 [M, K/32] bytes.
+// The same with MXFP4 codes: qx [M, K/2] E2M1 patterns; E8M0 scale bytes
+// row-major sx_e8m0 [M, K/32] (sx_rows = 0) or k-tiled [ceil(K/256)][sx_rows][8]
+// (sx_rows >= M, even), the layout the block-scaled GEMM reads.
 hipError_t launch_smooth_quant_lora_down_mx(const uint16_t* X, int M, int K, int r,
                                             const float* smooth, const uint16_t* L1, uint8_t* qx,
                                             uint8_t* sx_e8m0, float* T, bool one_slice,
-                                            hipStream_t stream);
+                                            int sx_rows, hipStream_t stream);
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
 // (lgkmcnt) and leaves its global loads in flight.  __syncthreads also waits
@@ -82,7 +86,9 @@ hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, 
                             float* part, int act, hipStream_t stream);
 
 // k2, MXFP4 variant: Y = act(block-scaled FP4 product + T L2^T + b), bf16 out.
-hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, const float* T,
+// Both scale operands are k-tiled: sx_e8m0 [ceil(K/256)][sx_rows][8] and
+// w_e8m0 [ceil(K/256)][N][8].
+hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_rows, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
                              uint16_t* Y, int act, hipStream_t stream);

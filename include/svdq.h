@@ -193,12 +193,30 @@ svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int 
  * share one E8M0 scale byte (2^(byte - 127), exponent floor(log2 amax) - 2)
  * and every element is an FP4 E2M1 number (nearest, ties to even,
  * saturating at +-6, sign kept).  Codes are packed like the int4 ones (two per
- * byte, even channel in the low nibble); scales are E8M0 bytes [rows, K/32].
+ * byte, even channel in the low nibble).  Scales are E8M0 bytes in one of two
+ * layouts:
+ *   row-major  [rows, K/32]: what the packer and svdq_quantize_activations_mxfp4
+ *              write, and what parity is defined on;
+ *   k-tiled    [ceil(K/256)][rows][8]: byte (t * rows + n) * 8 + j is the scale
+ *              of block 8 t + j of row n, blocks past K/32 are padding (127).
+ *              The forward's GEMM reads its weight scales in this layout: one
+ *              256-channel stage of a tile's rows is then one contiguous run.
+ *              svdq_mxfp4_tile_scales converts, once per weight.
  * The GEMM runs on CDNA4's block-scaled FP4 MFMA.  Requirements as for the
  * int4 entry points, with K % 128 == 0. */
 
-/* Stage three with MXFP4 on the host: Wq [N, K/2] and w_e8m0 [N, K/32] of
- * R = W diag(s) - L2 L1 (R formed exactly as for svdq_quantize_residual). */
+/* Bytes of the k-tiled layout of `rows` rows: ceil(K/256) * rows * 8; 0 if
+ * rows < 1 or K is not a positive multiple of 128. */
+size_t svdq_mxfp4_tiled_scale_bytes(int rows, int K);
+
+/* Row-major scales [rows, K/32] -> k-tiled (svdq_mxfp4_tiled_scale_bytes bytes,
+ * caller-allocated host memory; padding bytes are 127).  Host, synchronous.
+ * SVDQ_ERR_INVALID_ARG for NULL pointers or the shapes rejected above. */
+svdq_status svdq_mxfp4_tile_scales(const uint8_t* scales, int rows, int K, uint8_t* tiled);
+
+/* Stage three with MXFP4 on the host: Wq [N, K/2] and row-major w_e8m0
+ * [N, K/32] of R = W diag(s) - L2 L1 (R formed exactly as for
+ * svdq_quantize_residual).  The forward takes the scales k-tiled. */
 svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const float* smooth,
                                          const uint16_t* L1, const uint16_t* L2, int r,
                                          uint8_t* Wq, uint8_t* w_e8m0);
@@ -207,8 +225,9 @@ svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const flo
 size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r);
 
 /* The MXFP4 forward: quantize + lora_down, then the block-scaled GEMM whose
- * epilogue adds the lora_up product and the bias.  Device memory, asynchronous
- * on `stream`, no allocation. */
+ * epilogue adds the lora_up product and the bias.  w_e8m0 is k-tiled
+ * [ceil(K/256)][N][8] (see above); the workspace holds the activation scales
+ * k-tiled too.  Device memory, asynchronous on `stream`, no allocation. */
 svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
                                       const float* smooth, const uint16_t* L1,
                                       const uint16_t* L2, const uint8_t* Wq,

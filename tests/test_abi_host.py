@@ -245,9 +245,36 @@ def test_quantize_residual_mxfp4_bit_exact(name, rank):
 
 
 def test_workspace_bytes_mxfp4():
+    """qx | activation scales k-tiled [ceil(K/256)][M rounded up to even][8] | T slices."""
     al = lambda x: (x + 255) // 256 * 256
     M, K, N, r = 4096, 3072, 3072, 32
     b = S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r)
     assert b == al(M * K // 2) + al(M * K // 32) + al(2 * M * r * 4)
+    M, K = 77, 640                                                     # odd M, K % 256 == 128
+    assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 48, 0) == al(M * K // 2) + al(3 * 78 * 8)
     assert S.svdq_forward_workspace_bytes_mxfp4(M, 64, N, r) == 0     # K must be a multiple of 128
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 40, r) == 0
+
+
+@pytest.mark.parametrize("rows,K", [(48, 3072), (7, 640), (1, 128), (16, 384)])
+def test_mxfp4_tile_scales_layout(rows, K):
+    """The k-tiled scale layout: byte (t * rows + n) * 8 + j holds block 8 t + j of row n, and
+    the blocks past K/32 of the last tile are 127 -- a numpy re-indexing of the row-major bytes."""
+    sc = np.random.default_rng(rows + K).integers(0, 256, (rows, K // 32), dtype=np.uint8)
+    t = S.svdq_mxfp4_tile_scales(sc)
+    nt = (K + 255) // 256
+    assert t.shape == (nt, rows, 8)
+    assert S.svdq_mxfp4_tiled_scale_bytes(rows, K) == t.nbytes
+    padded = np.full((rows, 8 * nt), 127, np.uint8)
+    padded[:, :K // 32] = sc
+    np.testing.assert_array_equal(t, padded.reshape(rows, nt, 8).transpose(1, 0, 2))
+    flat = t.reshape(-1)
+    n, b = rows - 1, K // 32 - 1                                       # last row, last block
+    assert flat[((b // 8) * rows + n) * 8 + b % 8] == sc[n, b]
+
+
+def test_mxfp4_tile_scales_rejects():
+    assert S.svdq_mxfp4_tiled_scale_bytes(0, 128) == 0
+    assert S.svdq_mxfp4_tiled_scale_bytes(4, 64) == 0
+    with pytest.raises(S.SvdqError):
+        S.svdq_mxfp4_tile_scales(np.zeros((4, 3), np.uint8))          # K = 96

@@ -39,7 +39,12 @@ def with_lora(name, mx=False):
 
 
 def layer_to_device(p):
-    return dict(s=dev(p["s"]), L1=dev(p["L1"]), L2=dev(p["L2"]), Wq=dev(p["Wq"]), ws=dev(p["w_scales"]),
+    """Device copies of a packed layer; MXFP4 weight scales (E8M0 bytes) go k-tiled, as the
+    forward reads them."""
+    ws = p["w_scales"]
+    if ws.dtype == np.uint8:
+        ws = S.svdq_mxfp4_tile_scales(ws)
+    return dict(s=dev(p["s"]), L1=dev(p["L1"]), L2=dev(p["L2"]), Wq=dev(p["Wq"]), ws=dev(ws),
                 b=dev(p["b"]))
 
 

@@ -57,7 +57,9 @@ def packed_mx(name, M=None, K=None, N=None, rank=None):
     A = O.act_absmax(synth.calibration_activations(w)[:, :K])
     pk = O.pack_weights(W, A, w.alpha, rank=r)
     Wq, we = O.quantize_residual_mx(W, pk["s"], pk["L1"], pk["L2"])
-    p = dict(X=X, b=b, M=M, K=K, N=N, r=r, s=pk["s"], L1=pk["L1"], L2=pk["L2"], Wq=Wq, we=we)
+    # the oracle takes row-major scales, the forward k-tiled ones
+    p = dict(X=X, b=b, M=M, K=K, N=N, r=r, s=pk["s"], L1=pk["L1"], L2=pk["L2"], Wq=Wq, we=we,
+             we_tiled=S.svdq_mxfp4_tile_scales(we))
     _CACHE[key] = p
     return p
 
@@ -78,7 +80,7 @@ def run_forward(p):
     Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
     ws = torch.empty(S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r), dtype=torch.uint8, device=DEV)
     S.svdq_linear_forward_mxfp4(dev(p["X"]), dev(p["s"]), dev(p["L1"]) if r else None,
-                                dev(p["L2"]) if r else None, dev(p["Wq"]), dev(p["we"]), dev(p["b"]), Y, ws)
+                                dev(p["L2"]) if r else None, dev(p["Wq"]), dev(p["we_tiled"]), dev(p["b"]), Y, ws)
     torch.cuda.synchronize()
     return O.bf16_to_f64(Y.cpu().numpy().view(np.uint16))
 
@@ -165,7 +167,7 @@ def test_forward_mx_long_token_batch_sampled_rows():
     S.svdq_quantize_activations_mxfp4(Xd, sd, L1d, qx, sx, T)
     Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
     ws = torch.empty(S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r), dtype=torch.uint8, device=DEV)
-    S.svdq_linear_forward_mxfp4(Xd, sd, L1d, dev(p["L2"]), dev(p["Wq"]), dev(p["we"]), dev(p["b"]), Y, ws)
+    S.svdq_linear_forward_mxfp4(Xd, sd, L1d, dev(p["L2"]), dev(p["Wq"]), dev(p["we_tiled"]), dev(p["b"]), Y, ws)
     torch.cuda.synchronize()
     qx_o, sx_o, T_o = O.quantize_activations_mx(p["X"][rows], p["s"], p["L1"])[:3]
     np.testing.assert_array_equal(qx[ridx].cpu().numpy(), qx_o)
