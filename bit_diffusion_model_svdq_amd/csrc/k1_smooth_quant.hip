@@ -111,6 +111,12 @@ __host__ __device__ inline size_t lds_main_bytes(int rtm, int gslice) {
   return (size_t)gslice * kGroup * 4 + (size_t)16 * rtm * code_pitch(gslice) +
          (size_t)16 * rtm * gslice * 4;
 }
+// T partials [waves][16 rtm][r] floats: after the main part when the budget
+// allows (then written before the final barrier), else over it.
+__host__ __device__ inline size_t tpart_bytes(int rtm, int r) { return (size_t)kW * 16 * rtm * r * 4; }
+__host__ __device__ inline size_t t_own_offset(int rtm, int gslice) {
+  return (lds_main_bytes(rtm, gslice) + 15) & ~size_t(15);
+}
 
 // RT = r / 16 rank tiles; RTM row tiles per workgroup; gslice groups per K-slice.
 template <int RT, int RTM, bool MX>
@@ -136,7 +142,8 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   uint8_t* lcodes = reinterpret_cast<uint8_t*>(lds + gslice * kGroup);
   // per row and group: the float32 scale's bits (int4) or the two E8M0 bytes (MX)
   uint32_t* lscales = reinterpret_cast<uint32_t*>(lcodes + 16 * RTM * code_pitch(gslice));
-  float* tpart = lds;                             // reused after the codes have left
+  const bool t_own = t_own_offset(RTM, gslice) + tpart_bytes(RTM, r) <= kLdsBudget;
+  float* tpart = t_own ? lds + t_own_offset(RTM, gslice) / 4 : lds;
 
   const int m0 = blockIdx.x * 16 * RTM;
   const int fr = lane & 15;
@@ -336,9 +343,22 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     }
   }
 
+  // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + i.
+  // T partials [wave][row of the block][rank], summed over waves in order.
+  constexpr int RB = 16 * RTM;
+  auto write_tpart = [&] {
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int t = 0; t < RTM; ++t)
+#pragma unroll
+        for (int j = 0; j < RT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            tpart[(wave * RB + 16 * t + 4 * fk + i) * r + 16 * j + fr] = acc[t][j][i];
+    }
+  };
   // codes and scales of the block's rows for the slice, as whole row segments
-  __syncthreads();
-  {
+  auto store_codes = [&] {
     const int ng = sg1 - sg0;
     const int chunks = 2 * ng;                      // 16-byte pieces per row
     for (int e = tid; e < 16 * RTM * chunks; e += kThreads) {
@@ -363,34 +383,42 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
         }
       }
     }
-  }
-
-  if constexpr (RT > 0) {
-    // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + i.
-    // Partials [wave][row of the block][rank], summed over waves in order.
-    constexpr int RB = 16 * RTM;
-    float* Ts = T + (size_t)slice * M * r;
-    __syncthreads();                                // LDS is reused for the partials
+  };
+  auto reduce_t = [&] {
+    if constexpr (RT > 0) {
+      float* Ts = T + (size_t)slice * M * r;
+      for (int e = tid; e < RB * r; e += kThreads) {
+        const int rr = e / r, c = e - (e / r) * r;
+        float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < RTM; ++t)
-#pragma unroll
-      for (int j = 0; j < RT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          tpart[(wave * RB + 16 * t + 4 * fk + i) * r + 16 * j + fr] = acc[t][j][i];
-    __syncthreads();
-    for (int e = tid; e < RB * r; e += kThreads) {
-      const int rr = e / r, c = e - (e / r) * r;
-      float s = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < kW; ++wv) s += tpart[(wv * RB + rr) * r + c];
-      if (m0 + rr < M) Ts[(size_t)(m0 + rr) * r + c] = s;
+        for (int wv = 0; wv < kW; ++wv) s += tpart[(wv * RB + rr) * r + c];
+        if (m0 + rr < M) Ts[(size_t)(m0 + rr) * r + c] = s;
+      }
+    }
+  };
+  // The barriers order LDS only: the code stores need not land before the
+  // partial sums are read.  With its own LDS region, T's partials go in
+  // before the one barrier, and codes and T leave together.
+  if (t_own) {
+    write_tpart();
+    lds_barrier();
+    store_codes();
+    reduce_t();
+  } else {
+    lds_barrier();
+    store_codes();
+    if constexpr (RT > 0) {
+      lds_barrier();                                // the codes are read; LDS is reused
+      write_tpart();
+      lds_barrier();
+      reduce_t();
     }
   }
 }
 
 size_t lds_bytes(int rtm, int gslice, int r) {
-  return std::max(lds_main_bytes(rtm, gslice), (size_t)kW * 16 * rtm * r * 4);
+  const size_t own = t_own_offset(rtm, gslice) + tpart_bytes(rtm, r);
+  return own <= kLdsBudget ? own : std::max(lds_main_bytes(rtm, gslice), tpart_bytes(rtm, r));
 }
 
 template <int RT, int RTM, bool MX>

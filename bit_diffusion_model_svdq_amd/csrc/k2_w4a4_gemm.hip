@@ -121,9 +121,9 @@ __device__ inline int xcd_compact(int b, int count) {
 // workgroups, tile numbers [full, full + rem) are cut along K into `splits`
 // shares.  MODE kWhole: block b computes whole tile number b (of `full`).
 // MODE kShares: block u computes share u / rem of tile full + u % rem and
-// stores its raw fp32 accumulators in `part`.  MODE kFixup: block t sums the
-// shares of tile full + t in split order (deterministic) and runs the tail.
-constexpr int kWhole = 0, kShares = 1, kFixup = 2;
+// stores its raw fp32 accumulators in `part`.  w4a4_fixup_kernel sums them.
+constexpr int kWhole = 0, kShares = 1;
+constexpr int kMaxSplits = 8;      // K-shares per remainder tile, at most
 
 template <class C, bool EXPORT, int MODE>
 __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
@@ -147,8 +147,6 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   int s_begin = 0, s_end = stages;    // kShares: this share's stages
   if (MODE == kWhole) {
     tile_of_id(ntm, ntn, xcd_compact(blockIdx.x, full), tmi, tni);
-  } else if (MODE == kFixup) {
-    tile_of_id(ntm, ntn, full + blockIdx.x, tmi, tni);
   } else {
     const int tr = blockIdx.x % rem, sp = blockIdx.x / rem;
     tile_of_id(ntm, ntn, full + tr, tmi, tni);
@@ -357,7 +355,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
         __syncthreads();
       }
     }
-  } else if (MODE != kFixup) {
+  } else {
     // Stages sb+1 .. sb+PF wait in registers while stage sb is in LDS; after
     // each stage the next one goes to LDS and its slot takes the stage PF
     // further.  The barrier waits for the LDS stores only: the loads in
@@ -403,23 +401,6 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       }
     return;
   }
-  if (MODE == kFixup) {
-    for (int sp = 0; sp < splits; ++sp) {
-      const float4* src = reinterpret_cast<const float4*>(part) +
-                          (size_t)(blockIdx.x * splits + sp) * NACC * C::THREADS + tid;
-#pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) {
-          const float4 v = src[(size_t)(tm * C::TN + tn) * C::THREADS];
-          acc[tm][tn][0] += v.x;
-          acc[tm][tn][1] += v.y;
-          acc[tm][tn][2] += v.z;
-          acc[tm][tn][3] += v.w;
-        }
-    }
-  }
-
   // ---- epilogue: 1/256, + b + T L2^T (bf16 hi/lo MFMA), bf16 store
   if constexpr (kLastInTail) {
     tail::lowrank_bias_add<C::TM, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1,
@@ -446,6 +427,74 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 
   uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
   tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
+      acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
+      [&](int row) { return otile + row * C::BN; }, act);
+}
+
+// Fixup of the remainder split.  Block (t, wm) covers the 64-row band wm of
+// remainder tile full + t at the tile's full width: its waves stand in for
+// the band's (16-row slice, wave column) pairs, and each sums its accumulator
+// entries over the shares in split order, all of its loads issued at once.
+// The sums, the 1/256, the low-rank tail and the store are those the tile's
+// own waves would run, element for element.  rem x WM blocks spread over the
+// chip what rem blocks of a whole tile each would otherwise read alone.
+template <class C>
+__global__ __launch_bounds__(64 * C::TM * C::WN) void w4a4_fixup_kernel(
+    const float* __restrict__ part, int full, int splits, const float* __restrict__ T,
+    int t_slices, long t_stride, int r, const uint16_t* __restrict__ L2,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int row0, int row1,
+    int col0, int col1, int act) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NACC = C::TM * C::TN;
+  constexpr int BAND = 16 * C::TM;                  // rows of a wave's sub-tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int slice = wave % C::TM;                   // the 16-row slice tm of the sub-tile
+  const int wn = wave / C::TM;                      // the wave column it stands in for
+  const int wm = blockIdx.x % C::WM;
+  const int tr = blockIdx.x / C::WM;
+  const int ntm = (row1 - row0 + C::BM - 1) / C::BM;
+  const int ntn = (col1 - col0 + C::BN - 1) / C::BN;
+  int tmi, tni;
+  tile_of_id(ntm, ntn, full + tr, tmi, tni);
+  const int m0 = row0 + tmi * C::BM + wm * BAND;    // the band
+  const int n0 = col0 + tni * C::BN;
+  const int src_tid = (wm * C::WN + wn) * 64 + lane;  // the share writer's thread
+
+  f32x4 acc[1][C::TN];
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) acc[0][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float4* src = reinterpret_cast<const float4*>(part) +
+                      (size_t)tr * splits * NACC * C::THREADS +
+                      (size_t)slice * C::TN * C::THREADS + src_tid;
+  // at most kMaxSplits shares: every load is issued before the first add
+  // (clamped, unconditional); the adds run in split order for the real ones
+  float4 v[kMaxSplits][C::TN];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+      v[sp][tn] = src[((size_t)min(sp, splits - 1) * NACC + tn) * C::THREADS];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < splits)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        acc[0][tn][0] += v[sp][tn].x;
+        acc[0][tn][1] += v[sp][tn].y;
+        acc[0][tn][2] += v[sp][tn].z;
+        acc[0][tn][3] += v[sp][tn].w;
+      }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][tn][i] *= (1.0f / 256.0f);
+  const int wr = 16 * slice, wc = wn * C::TN * 16;
+  tail::lowrank_bias_add<1, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1, col1,
+                                      wr, wc, lane, 1.0f, [] {});
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  tail::store_tile<1, C::TN, BAND, C::BN, 64 * C::TM * C::WN>(
       acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
       [&](int row) { return otile + row * C::BN; }, act);
 }
@@ -509,7 +558,7 @@ SplitPlan plan_split(int M, int N, int K) {
   const int rem = tiles % cus;
   if (C::BM * C::BN < TileBig::BM * TileBig::BN || tiles < cus || rem == 0 || 4 * rem > cus)
     return p;
-  const int splits = std::min(std::min(8, cus / rem), stages);
+  const int splits = std::min(std::min(kMaxSplits, cus / rem), stages);
   if (splits < 2) return p;
   p.full = tiles - rem;
   p.rem = rem;
@@ -543,16 +592,14 @@ hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t
   e = hipGetLastError();
   if (EXPORT || e != hipSuccess || plan.rem == 0) return e;
   if ((e = set_lds_attr<C, false, kShares>()) != hipSuccess) return e;
-  if ((e = set_lds_attr<C, false, kFixup>()) != hipSuccess) return e;
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kShares>), dim3(plan.rem * plan.splits),
                      dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
                      ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part,
                      t_slices, (long)(row1 - row0) * r, act);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kFixup>), dim3(plan.rem), dim3(C::THREADS),
-                     C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
-                     col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
-                     (long)(row1 - row0) * r, act);
+  hipLaunchKernelGGL((w4a4_fixup_kernel<C>), dim3(plan.rem * C::WM), dim3(64 * C::TM * C::WN),
+                     16 * C::TM * C::BN * 2, stream, part, plan.full, plan.splits, T, t_slices,
+                     (long)(row1 - row0) * r, r, L2, bias, Y, ldy, row0, row1, col0, col1, act);
   return hipGetLastError();
 }
 
