@@ -192,3 +192,75 @@ def test_forward_mx_ragged_shapes(M, K, N, r):
     Yg = run_forward(p)
     Yref = O.forward_mx(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["we"], p["b"])
     check_y(Yg, Yref, f"mx ragged {M}x{K}x{N} r={r}")
+
+
+def forward_parts_mx(p):
+    M, K, N, r = p["M"], p["K"], p["N"], p["r"]
+    d = dict(X=dev(p["X"]), s=dev(p["s"]), L1=dev(p["L1"]) if r else None, L2=dev(p["L2"]) if r else None,
+             Wq=dev(p["Wq"]), we=dev(p["we_tiled"]), b=dev(p["b"]))
+    ws = torch.empty(S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r), dtype=torch.uint8, device=DEV)
+    return d, ws
+
+
+def test_forward_mx_stages_match_fused_call():
+    """svdq_forward_quantize_mxfp4 then svdq_forward_gemm_mxfp4 (the workspace carries the
+    k-tiled activation scales between them) equal the fused call bit for bit."""
+    say("mx stages vs fused smallk_640")
+    p = packed_mx("smallk_640")
+    M, K, N, r = p["M"], p["K"], p["N"], p["r"]
+    Yf = run_forward(p)
+    d, ws = forward_parts_mx(p)
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    S.svdq_forward_quantize_mxfp4(d["X"], d["s"], d["L1"], ws)
+    S.svdq_forward_gemm_mxfp4(M, K, d["L2"], d["Wq"], d["we"], d["b"], Y, ws, r)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(O.bf16_to_f64(Y.cpu().numpy().view(np.uint16)), Yf)
+
+
+def test_forward_mx_in_hip_graph_replays_match_eager():
+    """The MXFP4 forward captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, reproduces the eager output bit for bit."""
+    say("mx graph replay smallk_1280")
+    p = packed_mx("smallk_1280")
+    M, N = p["M"], p["N"]
+    Y_eager = run_forward(p)
+    d, ws = forward_parts_mx(p)
+    Yg = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    fwd = lambda: S.svdq_linear_forward_mxfp4(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["we"], d["b"], Yg, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for rep in range(3):
+        Yg.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(O.bf16_to_f64(Yg.cpu().numpy().view(np.uint16)), Y_eager,
+                                      err_msg=f"replay {rep}")
+        run_forward(p)              # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K", [(77, 640), (256, 1024)])
+def test_k1_mx_workspace_scales_k_tiled(M, K):
+    """The forward's workspace: codes [M, K/2] first, then the E8M0 scales k-tiled
+    [ceil(K/256)][M rounded up to even][8] -- bit-exact against the oracle's row-major
+    bytes re-indexed (an odd M and K % 256 == 128 exercise the row pitch and the tail)."""
+    say(f"k1 mx workspace layout {M}x{K}")
+    p = packed_mx("tiny", M=M, K=K, N=64, rank=16)
+    d, ws = forward_parts_mx(p)
+    S.svdq_forward_quantize_mxfp4(d["X"], d["s"], d["L1"], ws)
+    torch.cuda.synchronize()
+    qx_o, sx_o, _, _ = O.quantize_activations_mx(p["X"], p["s"], p["L1"])
+    w = ws.cpu().numpy()
+    qbytes = (M * K // 2 + 255) // 256 * 256
+    np.testing.assert_array_equal(w[:M * K // 2].reshape(M, K // 2), qx_o)
+    rows, nt, nb = M + (M & 1), (K + 255) // 256, K // 32
+    tiled = w[qbytes:qbytes + nt * rows * 8].reshape(nt, rows, 8)
+    got = tiled[:, :M, :].transpose(1, 0, 2).reshape(M, nt * 8)[:, :nb]
+    np.testing.assert_array_equal(got, sx_o)
