@@ -16,19 +16,21 @@
 // 2i in the low nibble of byte i -- the canonical packed row order -- and the
 // scale byte of that 32-channel block in the low byte of its scale register.
 //
-// Data path: two 128-channel steps per pipeline stage; the stage's A and B
-// rows (128 bytes each) and scale bytes (8 per row) are copied from global
-// memory straight into LDS (global_load_lds: no registers, no ALU), double
-// buffered.  Both scale operands come k-tiled ([ceil(K/256)][rows][8]): a
-// tile's scales of one stage are then one contiguous run, 1 KB per copy,
-// where row-major [rows, K/32] scales would cost one 8-byte piece per row.  The compiler makes every LDS read wait for all copies in flight
-// (it cannot tell the two buffers apart), so a wave first reads all of its
-// fragments and scales of the stage, then issues its copies of the next stage,
-// then runs the stage's 2 x TM x TN MFMAs while the copies travel.
-//
-// The 16-byte chunks of a row are XOR-swizzled (see swz_key); the direct copy
-// writes lane-linear LDS addresses, so each lane fetches the global chunk that
-// belongs at its LDS position.
+// Data path: a ring of NR LDS buffers, one 128-channel step each, filled
+// straight from global memory (global_load_lds: no registers, no ALU) NR - 1
+// steps ahead of the MFMAs, so that the copies' latency hides behind several
+// steps of work.  A buffer holds the step's A and B rows (64 bytes each,
+// 16-byte chunks XOR-swizzled by row so that a fragment read spreads over the
+// banks) and the tile's scale bytes of the step pair.  Both scale operands
+// come k-tiled ([ceil(K/256)][rows][8]), so those are one contiguous run per
+// tile and move as 1 KB copies; a step uses the low or high 4 bytes of each
+// row's 8.  Every wave issues the same number of copies per step (the last is
+// repeated to even them out), so s_waitcnt vmcnt waits for exactly this
+// wave's copies of the step while the later steps' stay in flight; a plain
+// s_barrier then makes everyone's copies visible (__syncthreads would wait
+// for all copies in flight).  Each buffer is its own __shared__ array: the
+// compiler then knows that reading one buffer does not depend on the copies
+// into another and issues no wait for them.
 //
 // The low-rank branch's up projection T L2^T initializes the accumulators
 // before the main loop (its loads are issued together, without branches, right
@@ -44,11 +46,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int KS = 128;           // channels per MFMA
-constexpr int SK = 2;             // MFMA k-steps per pipeline stage
-constexpr int ROWB = SK * KS / 2; // FP4 bytes per row and stage (128)
-constexpr int SROWB = SK * KS / 32; // scale bytes per row and stage (8)
-constexpr int kFmtFp4 = 4;        // cbsz / blgp code of FP4 E2M1
+constexpr int KS = 128;             // channels per MFMA step
+constexpr int ROWB = KS / 2;        // FP4 bytes per row and step (64)
+constexpr int SROWB = 8;            // k-tiled scale bytes per row and pair of steps
+constexpr int NR = 4;               // ring buffers: NR - 1 steps of copies ahead
+constexpr int kFmtFp4 = 4;          // cbsz / blgp code of FP4 E2M1
 
 template <int WM_, int WN_, int TM_, int TN_>
 struct MxTile {
@@ -57,17 +59,19 @@ struct MxTile {
   static constexpr int BN = WN * TN * 16;
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int A_BYTES = BM * ROWB;
-  static constexpr int B_BYTES = BN * ROWB;
-  // scale bytes of a stage, rounded up to whole 1 KB copies (the rows past
-  // the tile that fill the rest are never read)
+  static constexpr int ROWS_BYTES = (BM + BN) * ROWB;   // A rows, then B rows
+  // scale bytes of the step pair, rounded up to whole 1 KB copies (the rows
+  // past the tile that fill the rest are never read)
   static constexpr int SA_BYTES = (BM * SROWB + 1023) / 1024 * 1024;
   static constexpr int SB_BYTES = (BN * SROWB + 1023) / 1024 * 1024;
-  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static constexpr int OUT = BM * BN * 2;
-  static constexpr int LDS = (2 * STAGE > OUT ? 2 * STAGE : OUT);
-  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB copies");
-  static_assert(SA_BYTES % 1024 == 0 && SB_BYTES % 1024 == 0, "whole 1 KB copies");
+  static constexpr int BUF = ROWS_BYTES + SA_BYTES + SB_BYTES;
+  static constexpr int ROW_COPIES = ROWS_BYTES / 1024;
+  static constexpr int COPIES = ROW_COPIES + (SA_BYTES + SB_BYTES) / 1024;   // per step
+  static constexpr int CPW = (COPIES + WAVES - 1) / WAVES;                   // per wave and step
+  static constexpr int OUT_ROWS = (BM + NR - 1) / NR;   // output rows staged per buffer
+  static_assert(ROWS_BYTES % 1024 == 0, "whole 1 KB row copies");
+  static_assert(OUT_ROWS * BN * 2 <= BUF, "the output tile fits the ring");
+  static_assert(CPW * (NR - 2) < 64, "vmcnt range");
 };
 
 using MxBig = MxTile<4, 2, 4, 6>;    // 256 x 192, 8 waves
@@ -89,28 +93,35 @@ __device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
   tn = in / gsize;
 }
 
-// The 8 chunks of a 128-byte row are XOR-swizzled by row % 8.  A fragment read
-// spans 16 consecutive rows starting at a multiple of 16, so the key depends on
-// the lane alone and every fragment of a wave shares one base address plus
-// immediate offsets; the LDS reports no bank conflicts for this pattern.
-__device__ inline int swz_key(int row) { return row & 7; }
-// byte offset of logical 16-byte chunk c of LDS row `row`
-__device__ inline int swz(int row, int c) { return row * ROWB + ((c ^ swz_key(row)) << 4); }
+// XOR key of the 16-byte chunks of a 64-byte LDS row: a fragment read covers
+// 16 consecutive rows (from a multiple of 16) and chunk l / 16 per lane; the
+// key (row / 2) % 4 spreads them over all banks.
+__device__ inline int swz_key(int row) { return (row >> 1) & 3; }
+
+// s_waitcnt with vmcnt = n, the other counters untouched
+template <int n>
+__device__ inline void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     const uint8_t* __restrict__ qx, const uint8_t* __restrict__ sx, int sx_rows,
     const float* __restrict__ T, int t_slices, long t_stride, int M, int K, int N, int r,
-    const uint16_t* __restrict__ L2,
-    const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ sw,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int act) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
+    const uint8_t* __restrict__ sw, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ Y, int act) {
+  static_assert(NR == 4, "the ring below names four buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[C::BUF];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int KB = K / 2;            // packed bytes per row
   const int ksteps = K / KS;
-  const int stages = (ksteps + SK - 1) / SK;
   const int ntm = (M + C::BM - 1) / C::BM;
   const int ntn = (N + C::BN - 1) / C::BN;
   int tmi, tni;
@@ -118,46 +129,44 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   const int m0 = tmi * C::BM;
   const int n0 = tni * C::BN;
 
-  auto stage_a = [&](int buf) { return lds + buf * C::STAGE; };
-  auto stage_b = [&](int buf) { return lds + buf * C::STAGE + C::A_BYTES; };
-  auto stage_sa = [&](int buf) { return lds + buf * C::STAGE + C::A_BYTES + C::B_BYTES; };
-  auto stage_sb = [&](int buf) { return stage_sa(buf) + C::SA_BYTES; };
-
-  // ---- global -> LDS copies of stage s.  A copy instruction moves 64 lanes x
-  // 16 bytes to consecutive LDS; lane j of copy q fills LDS byte q * 1024 + 16 j,
-  // i.e. row (q * 1024 + 16 j) / ROWB, physical chunk j % 8, and fetches the
-  // logical chunk that the swizzle puts there.  Rows past the matrix and the
-  // missing second step of an odd last stage re-read valid data, never used.
-  auto copy_rows = [&](const uint8_t* src, int nrows_total, int row_base, int ld, int s,
-                       uint8_t* dst, int bytes) {
-    const int jrow = lane >> 3, pch = lane & 7;
-    for (int q = wave; q < bytes / 1024; q += C::WAVES) {
-      const int row = q * (1024 / ROWB) + jrow;
-      int chunk = pch ^ swz_key(row);
-      if (s * SK + (chunk >> 2) >= ksteps) chunk &= 3;
-      const uint8_t* g = src + (size_t)min(row_base + row, nrows_total - 1) * ld + s * ROWB + chunk * 16;
-      __builtin_amdgcn_global_load_lds(g, (lds_ptr)(dst + q * 1024), 16, 0, 0);
+  // ---- this wave's copies of a step: copy q = wave + i WAVES (the last one
+  // repeated where the count does not divide), 1 KB each.  A row copy fills
+  // LDS rows 16 q .. + 15 (A rows, then B rows), lane j the physical chunk
+  // j % 4 of row 16 q + j / 4, fetched from the logical chunk the swizzle puts
+  // there.  A scale copy fills 1 KB of the A or B scale run of the step pair.
+  // Rows past the matrix re-read its last row, scale lanes past a run its last
+  // 16 bytes: never used.
+  const uint8_t* src[C::CPW];
+  int dst[C::CPW];
+  bool is_scale[C::CPW];
+  long pair_stride[C::CPW];      // scale copies: bytes from one step pair to the next
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i) {
+    const int q = min(wave + i * C::WAVES, C::COPIES - 1);
+    is_scale[i] = q >= C::ROW_COPIES;
+    if (!is_scale[i]) {
+      const int row = q * 16 + (lane >> 2);
+      const int chunk = (lane & 3) ^ swz_key(row);
+      src[i] = (row < C::BM ? qx + (size_t)min(m0 + row, M - 1) * KB
+                            : Wq + (size_t)min(n0 + row - C::BM, N - 1) * KB) + chunk * 16;
+      dst[i] = q * 1024;
+      pair_stride[i] = 0;
+    } else {
+      const int qs = q - C::ROW_COPIES;
+      const bool a = qs < C::SA_BYTES / 1024;
+      const int rows = a ? sx_rows : N;
+      const int base = (a ? m0 : n0) * SROWB + (a ? qs : qs - C::SA_BYTES / 1024) * 1024;
+      src[i] = (a ? sx : sw) + min(base + lane * 16, rows * SROWB - 16);
+      dst[i] = C::ROWS_BYTES + qs * 1024;
+      pair_stride[i] = (long)rows * SROWB;
     }
-  };
-  // Scales are k-tiled: stage s of rows [0, rows) is one run of 8 * rows
-  // bytes (rows even), so a tile's scales of a stage are contiguous and move
-  // as 1 KB copies of 16 bytes per lane.  Lanes past the run re-read its last
-  // 16 bytes, into LDS rows that are never read.  An odd last stage has no
-  // second step; its upper 4 bytes per row are never used.
-  auto copy_scales = [&](const uint8_t* src, int rows, int row_base, int s, uint8_t* dst,
-                         int bytes) {
-    const uint8_t* run = src + (size_t)s * rows * SROWB;
-    const int last = rows * SROWB - 16;
-    for (int q = wave; q < bytes / 1024; q += C::WAVES) {
-      const int off = min(row_base * SROWB + q * 1024 + lane * 16, last);
-      __builtin_amdgcn_global_load_lds(run + off, (lds_ptr)(dst + q * 1024), 16, 0, 0);
+  }
+  auto copy_step = [&](int s, uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const uint8_t* g = src[i] + (is_scale[i] ? (s >> 1) * pair_stride[i] : (long)s * ROWB);
+      __builtin_amdgcn_global_load_lds(g, (lds_ptr)(buf + dst[i]), 16, 0, 0);
     }
-  };
-  auto copy_stage = [&](int s, int buf) {
-    copy_rows(qx, M, m0, KB, s, stage_a(buf), C::A_BYTES);
-    copy_rows(Wq, N, n0, KB, s, stage_b(buf), C::B_BYTES);
-    copy_scales(sx, sx_rows, m0, s, stage_sa(buf), C::SA_BYTES);
-    copy_scales(sw, N, n0, s, stage_sb(buf), C::SB_BYTES);
   };
 
   const int wm = wave / C::WN, wn = wave - (wave / C::WN) * C::WN;
@@ -171,68 +180,84 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A stage from LDS: the fragments of both steps (16 bytes per lane each) and
-  // each row's 8 scale bytes, then the copies of the next stage, then the MFMAs.
-  // The scale of block fk in step ks is byte 4 ks + fk of the row's 8, moved to
-  // byte 0 of the MFMA's scale operand.
-  auto stage = [&](int buf, bool second, bool more, int s) {
-    const uint8_t* pa = stage_a(buf);
-    const uint8_t* pb = stage_b(buf);
-    const uint8_t* psa = stage_sa(buf);
-    const uint8_t* psb = stage_sb(buf);
-    uint4 af[SK][C::TM], bf[SK][C::TN];
-    uint2 sa[C::TM], sb[C::TN];
+  // Fragment addresses: tile t of a wave starts 16 rows further and the
+  // swizzle key of row 16 t + fr is that of fr, so every fragment of a kind is
+  // one lane base plus a compile-time offset.  The scale of block fk in step
+  // s is byte 4 (s % 2) + fk of the row's 8.
+  const int swz_lane = (fk ^ swz_key(fr)) << 4;
+  const int a_lane = (wr + fr) * ROWB + swz_lane;
+  const int b_lane = (C::BM + wc + fr) * ROWB + swz_lane;
+  const int sa_lane = C::ROWS_BYTES + (wr + fr) * SROWB + fk;
+  const int sb_lane = C::ROWS_BYTES + C::SA_BYTES + (wc + fr) * SROWB + fk;
+
+  // Step s: wait for this wave's copies of step s (those of s + 1, s + 2 stay
+  // in flight), barrier (everyone's have landed, and everyone is done with
+  // step s - 1), copy step s + NR - 1 into the buffer step s - 1 used (past
+  // the last step: a repeat of the last step, never read), then the step's
+  // fragments and MFMAs.
+  auto step = [&](int s, const uint8_t* cur, uint8_t* freed) {
+    wait_vmcnt<C::CPW * (NR - 2)>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    copy_step(min(s + NR - 1, ksteps - 1), freed);
+    __builtin_amdgcn_sched_barrier(0);   // the copies leave before the step's work
+    const int h = 4 * (s & 1);
+    uint4 af[C::TM], bf[C::TN];
+    int sa[C::TM], sb[C::TN];
 #pragma unroll
     for (int t = 0; t < C::TM; ++t) {
-      const int row = wr + 16 * t + fr;
-#pragma unroll
-      for (int ks = 0; ks < SK; ++ks)
-        af[ks][t] = *reinterpret_cast<const uint4*>(pa + swz(row, 4 * ks + fk));
-      sa[t] = *reinterpret_cast<const uint2*>(psa + row * SROWB);
+      af[t] = *reinterpret_cast<const uint4*>(cur + a_lane + t * 16 * ROWB);
+      sa[t] = cur[sa_lane + h + t * 16 * SROWB];
     }
 #pragma unroll
     for (int t = 0; t < C::TN; ++t) {
-      const int row = wc + 16 * t + fr;
-#pragma unroll
-      for (int ks = 0; ks < SK; ++ks)
-        bf[ks][t] = *reinterpret_cast<const uint4*>(pb + swz(row, 4 * ks + fk));
-      sb[t] = *reinterpret_cast<const uint2*>(psb + row * SROWB);
+      bf[t] = *reinterpret_cast<const uint4*>(cur + b_lane + t * 16 * ROWB);
+      sb[t] = cur[sb_lane + h + t * 16 * SROWB];
     }
-    if (more) copy_stage(s + 1, buf ^ 1);
 #pragma unroll
-    for (int ks = 0; ks < SK; ++ks) {
-      if (ks == 1 && !second) break;
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const v8i bv = v8i{(int)bf[tn].x, (int)bf[tn].y, (int)bf[tn].z, (int)bf[tn].w, 0, 0, 0, 0};
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) {
-        const int sbv = (int)((ks ? sb[tn].y : sb[tn].x) >> (8 * fk));
-        const uint4 b = bf[ks][tn];
-        const v8i bv = v8i{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) {
-          const int sav = (int)((ks ? sa[tm].y : sa[tm].x) >> (8 * fk));
-          const uint4 a = af[ks][tm];
-          const v8i av = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av, bv, acc[tm][tn], kFmtFp4, kFmtFp4, 0, sav, 0, sbv);
-        }
+      for (int tm = 0; tm < C::TM; ++tm) {
+        const v8i av = v8i{(int)af[tm].x, (int)af[tm].y, (int)af[tm].z, (int)af[tm].w, 0, 0, 0, 0};
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bv, acc[tm][tn], kFmtFp4, kFmtFp4, 0, sa[tm], 0, sb[tn]);
       }
     }
   };
 
+  // prologue: the first NR - 1 steps' copies leave with the low-rank loads
   tail::lowrank_bias_add<C::TM, C::TN, 0>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
-                                          N, wr, wc, lane, 1.0f, [&] { copy_stage(0, 0); });
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = 0; s < stages; ++s) {
-    stage(s & 1, s * SK + 1 < ksteps, s + 1 < stages, s);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of the next stage have landed
-    __syncthreads();                 // ... and everyone's; the current buffer is free
+                                          N, wr, wc, lane, 1.0f, [&] {
+    copy_step(0, ring0);
+    copy_step(min(1, ksteps - 1), ring1);
+    copy_step(min(2, ksteps - 1), ring2);
+  });
+  // whole turns of the ring without branches (so that the compiler's count of
+  // the copies in flight stays exact), then the last 0..3 steps
+  int s0 = 0;
+  for (; s0 + NR <= ksteps; s0 += NR) {
+    step(s0, ring0, ring3);
+    step(s0 + 1, ring1, ring0);
+    step(s0 + 2, ring2, ring1);
+    step(s0 + 3, ring3, ring2);
   }
+  if (s0 < ksteps) step(s0, ring0, ring3);
+  if (s0 + 1 < ksteps) step(s0 + 1, ring1, ring0);
+  if (s0 + 2 < ksteps) step(s0 + 2, ring2, ring1);
 
-  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  // every copy has landed and every wave is done with the ring
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
       acc, bias, Y, N, m0, n0, M, N, wr, wc, lane, tid,
-      [&](int row) { return otile + row * C::BN; }, act);
+      [&](int row) {
+        const int g = row / C::OUT_ROWS;
+        uint8_t* b = g == 0 ? ring0 : g == 1 ? ring1 : g == 2 ? ring2 : ring3;
+        return reinterpret_cast<uint16_t*>(b) + (row - g * C::OUT_ROWS) * C::BN;
+      },
+      act);
 }
 
 int cu_count_mx() {
@@ -258,14 +283,7 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, int sx_rows, const float
                   int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
                   const uint8_t* sw, const uint16_t* bias, uint16_t* Y, int act,
                   hipStream_t stream) {
-  static bool attr = false;  // benign race: every caller sets the same value
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mxfp4_gemm_kernel<C>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL(mxfp4_gemm_kernel<C>, dim3(tiles_of<C>(M, N)), dim3(C::THREADS), C::LDS,
+  hipLaunchKernelGGL(mxfp4_gemm_kernel<C>, dim3(tiles_of<C>(M, N)), dim3(C::THREADS), 0,
                      stream, qx, sx, sx_rows, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias,
                      Y, act);
   return hipGetLastError();
