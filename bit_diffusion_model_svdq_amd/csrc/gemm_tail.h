@@ -209,5 +209,99 @@ __device__ inline void store_tile(f32x4 (&acc)[TM][TN], const uint16_t* __restri
   }
 }
 
+// Tile coordinates of tile number `id`: rastered in groups of 8 token tiles.
+__device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
+  constexpr int GROUP_M = 8;
+  const int per_group = GROUP_M * ntn;
+  const int grp = id / per_group;
+  const int first = grp * GROUP_M;
+  const int gsize = min(ntm - first, GROUP_M);
+  const int in = id - grp * per_group;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; block b of `count` (a
+// multiple of 8) gets tile number (b % 8) * count / 8 + b / 8, so that each
+// XCD works on one compact run of tiles and keeps its operand rows in its L2.
+__device__ inline int xcd_compact(int b, int count) {
+  return (count & 7) == 0 ? (b & 7) * (count >> 3) + (b >> 3) : b;
+}
+
+// Remainder split of a GEMM: when the tile count leaves a last, nearly empty
+// wave of workgroups, the tiles [full, full + rem) are cut along K into at
+// most kMaxSplits shares, each storing its raw fp32 accumulators, thread by
+// thread ([tile * splits + share][TM * TN][THREADS] float4), and a fixup
+// pass sums them.
+constexpr int kMaxSplits = 8;
+
+// The fixup, for a tile of WM x WN waves of TM x TN 16x16 accumulators and
+// THREADS threads.  Block (t, wm) covers the 16 TM-row band wm of remainder
+// tile full + t at the tile's full width: its TM x WN waves stand in for the
+// band's (16-row slice, wave column) pairs, and each sums its accumulator
+// entries over the shares in split order, all of its loads issued at once.
+// Then `scale`, the bias and low-rank tail, and the store, as the tile's own
+// waves would run them.  rem x WM blocks spread over the chip what rem blocks
+// of whole tiles would each read alone.  Launch: rem * WM blocks of
+// 64 TM WN threads, 16 TM BN * 2 bytes of LDS.
+template <int TM, int TN, int WM, int WN, int BM, int BN, int THREADS>
+__device__ inline void split_fixup(const float* __restrict__ part, int full, int splits,
+                                   float scale, const float* __restrict__ T, int t_slices,
+                                   long t_stride, int r, const uint16_t* __restrict__ L2,
+                                   const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+                                   int ldy, int row0, int row1, int col0, int col1, int act,
+                                   uint8_t* lds) {
+  constexpr int NACC = TM * TN;
+  constexpr int BAND = 16 * TM;                     // rows of a wave's sub-tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int slice = wave % TM;                      // the 16-row slice tm of the sub-tile
+  const int wn = wave / TM;                         // the wave column it stands in for
+  const int wm = blockIdx.x % WM;
+  const int tr = blockIdx.x / WM;
+  const int ntm = (row1 - row0 + BM - 1) / BM;
+  const int ntn = (col1 - col0 + BN - 1) / BN;
+  int tmi, tni;
+  tile_of_id(ntm, ntn, full + tr, tmi, tni);
+  const int m0 = row0 + tmi * BM + wm * BAND;       // the band
+  const int n0 = col0 + tni * BN;
+  const int src_tid = (wm * WN + wn) * 64 + lane;   // the share writer's thread
+
+  f32x4 acc[1][TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) acc[0][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float4* src = reinterpret_cast<const float4*>(part) + (size_t)tr * splits * NACC * THREADS +
+                      (size_t)slice * TN * THREADS + src_tid;
+  // every load is issued before the first add (clamped, unconditional); the
+  // adds run in split order for the real shares
+  float4 v[kMaxSplits][TN];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      v[sp][tn] = src[((size_t)min(sp, splits - 1) * NACC + tn) * THREADS];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < splits)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        acc[0][tn][0] += v[sp][tn].x;
+        acc[0][tn][1] += v[sp][tn].y;
+        acc[0][tn][2] += v[sp][tn].z;
+        acc[0][tn][3] += v[sp][tn].w;
+      }
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][tn][i] *= scale;
+  const int wr = 16 * slice, wc = wn * TN * 16;
+  lowrank_bias_add<1, TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1, col1, wr, wc,
+                             lane, 1.0f, [] {});
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+  store_tile<1, TN, BAND, BN, 64 * TM * WN>(acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane,
+                                             tid, [&](int row) { return otile + row * BN; }, act);
+}
+
 }  // namespace tail
 }  // namespace svdq

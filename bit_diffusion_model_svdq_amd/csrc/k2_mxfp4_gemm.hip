@@ -78,20 +78,9 @@ using MxBig = MxTile<4, 2, 4, 6>;    // 256 x 192, 8 waves
 using MxMed = MxTile<2, 2, 4, 4>;    // 128 x 128, 4 waves
 using MxSmall = MxTile<2, 2, 2, 2>;  //  64 x  64, 4 waves
 
-__device__ inline int xcd_compact(int b, int count) {
-  return (count & 7) == 0 ? (b & 7) * (count >> 3) + (b >> 3) : b;
-}
-
-__device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
-  const int per_group = GROUP_M * ntn;
-  const int grp = id / per_group;
-  const int first = grp * GROUP_M;
-  const int gsize = min(ntm - first, GROUP_M);
-  const int in = id - grp * per_group;
-  tm = first + in % gsize;
-  tn = in / gsize;
-}
+using tail::tile_of_id;
+using tail::xcd_compact;
+using tail::kMaxSplits;
 
 // XOR key of the 16-byte chunks of a 64-byte LDS row: a fragment read covers
 // 16 consecutive rows (from a multiple of 16) and chunk l / 16 per lane; the
@@ -105,13 +94,20 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <class C>
+// MODE kWhole: block b computes whole tile number b of `full`.  MODE kShares
+// (remainder split, see tail::split_fixup): block u computes share u / rem of
+// tile full + u % rem, its steps only, and stores its raw accumulators in
+// `part`; the fixup adds the low-rank branch and the bias.
+constexpr int kWhole = 0, kShares = 1;
+
+template <class C, int MODE>
 __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
     const uint8_t* __restrict__ qx, const uint8_t* __restrict__ sx, int sx_rows,
     const float* __restrict__ T, int t_slices, long t_stride, int M, int K, int N, int r,
     const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ sw, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ Y, int act) {
+    uint16_t* __restrict__ Y, int act, int full, int rem, int splits,
+    float* __restrict__ part) {
   static_assert(NR == 4, "the ring below names four buffers");
   __shared__ __attribute__((aligned(16))) uint8_t ring0[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t ring1[C::BUF];
@@ -125,7 +121,17 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   const int ntm = (M + C::BM - 1) / C::BM;
   const int ntn = (N + C::BN - 1) / C::BN;
   int tmi, tni;
-  tile_of_id(ntm, ntn, xcd_compact(blockIdx.x, ntm * ntn), tmi, tni);
+  int sb = 0, se = ksteps, unit = 0;     // this block's steps; kShares: its slot in `part`
+  if (MODE == kWhole) {
+    tile_of_id(ntm, ntn, xcd_compact(blockIdx.x, full), tmi, tni);
+  } else {
+    const int tr = blockIdx.x % rem, sp = blockIdx.x / rem;
+    tile_of_id(ntm, ntn, full + tr, tmi, tni);
+    unit = tr * splits + sp;
+    sb = (int)((long)ksteps * sp / splits);
+    se = (int)((long)ksteps * (sp + 1) / splits);
+  }
+  const int nsteps = se - sb;
   const int m0 = tmi * C::BM;
   const int n0 = tni * C::BN;
 
@@ -190,16 +196,17 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   const int sa_lane = C::ROWS_BYTES + (wr + fr) * SROWB + fk;
   const int sb_lane = C::ROWS_BYTES + C::SA_BYTES + (wc + fr) * SROWB + fk;
 
-  // Step s: wait for this wave's copies of step s (those of s + 1, s + 2 stay
-  // in flight), barrier (everyone's have landed, and everyone is done with
-  // step s - 1), copy step s + NR - 1 into the buffer step s - 1 used (past
-  // the last step: a repeat of the last step, never read), then the step's
-  // fragments and MFMAs.
-  auto step = [&](int s, const uint8_t* cur, uint8_t* freed) {
+  // Step sb + j: wait for this wave's copies of the step (those of the next
+  // two stay in flight), barrier (everyone's have landed, and everyone is done
+  // with step j - 1), copy step j + NR - 1 into the buffer step j - 1 used
+  // (past the last step: a repeat of the last step, never read), then the
+  // step's fragments and MFMAs.
+  auto step = [&](int j, const uint8_t* cur, uint8_t* freed) {
+    const int s = sb + j;
     wait_vmcnt<C::CPW * (NR - 2)>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    copy_step(min(s + NR - 1, ksteps - 1), freed);
+    copy_step(sb + min(j + NR - 1, nsteps - 1), freed);
     __builtin_amdgcn_sched_barrier(0);   // the copies leave before the step's work
     const int h = 4 * (s & 1);
     uint4 af[C::TM], bf[C::TN];
@@ -227,29 +234,46 @@ __global__ __launch_bounds__(C::THREADS) void mxfp4_gemm_kernel(
   };
 
   // prologue: the first NR - 1 steps' copies leave with the low-rank loads
-  tail::lowrank_bias_add<C::TM, C::TN, 0>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
-                                          N, wr, wc, lane, 1.0f, [&] {
-    copy_step(0, ring0);
-    copy_step(min(1, ksteps - 1), ring1);
-    copy_step(min(2, ksteps - 1), ring2);
-  });
+  // (shares leave the low-rank branch to the fixup)
+  auto first_copies = [&] {
+    copy_step(sb, ring0);
+    copy_step(sb + min(1, nsteps - 1), ring1);
+    copy_step(sb + min(2, nsteps - 1), ring2);
+  };
+  if (MODE == kWhole)
+    tail::lowrank_bias_add<C::TM, C::TN, 0>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
+                                            N, wr, wc, lane, 1.0f, first_copies);
+  else
+    first_copies();
   // whole turns of the ring without branches (so that the compiler's count of
   // the copies in flight stays exact), then the last 0..3 steps
-  int s0 = 0;
-  for (; s0 + NR <= ksteps; s0 += NR) {
-    step(s0, ring0, ring3);
-    step(s0 + 1, ring1, ring0);
-    step(s0 + 2, ring2, ring1);
-    step(s0 + 3, ring3, ring2);
+  int j0 = 0;
+  for (; j0 + NR <= nsteps; j0 += NR) {
+    step(j0, ring0, ring3);
+    step(j0 + 1, ring1, ring0);
+    step(j0 + 2, ring2, ring1);
+    step(j0 + 3, ring3, ring2);
   }
-  if (s0 < ksteps) step(s0, ring0, ring3);
-  if (s0 + 1 < ksteps) step(s0 + 1, ring1, ring0);
-  if (s0 + 2 < ksteps) step(s0 + 2, ring2, ring1);
+  if (j0 < nsteps) step(j0, ring0, ring3);
+  if (j0 + 1 < nsteps) step(j0 + 1, ring1, ring0);
+  if (j0 + 2 < nsteps) step(j0 + 2, ring2, ring1);
 
-  // every copy has landed and every wave is done with the ring
+  // every copy has landed (a workgroup may not leave copies into its LDS
+  // behind) and every wave is done with the ring
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if (MODE == kShares) {
+    float4* dst = reinterpret_cast<float4*>(part) + (size_t)unit * C::TM * C::TN * C::THREADS + tid;
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) {
+        const f32x4 a = acc[tm][tn];
+        dst[(size_t)(tm * C::TN + tn) * C::THREADS] = make_float4(a[0], a[1], a[2], a[3]);
+      }
+    return;
+  }
   tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
       acc, bias, Y, N, m0, n0, M, N, wr, wc, lane, tid,
       [&](int row) {
@@ -278,29 +302,88 @@ int tiles_of(int rows, int cols) {
   return ((rows + C::BM - 1) / C::BM) * ((cols + C::BN - 1) / C::BN);
 }
 
+// Fixup of the remainder split (tail::split_fixup); the accumulators are the sums.
+template <class C>
+__global__ __launch_bounds__(64 * C::TM * C::WN) void mxfp4_fixup_kernel(
+    const float* __restrict__ part, int full, int splits, const float* __restrict__ T,
+    int t_slices, long t_stride, int r, const uint16_t* __restrict__ L2,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int act) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  tail::split_fixup<C::TM, C::TN, C::WM, C::WN, C::BM, C::BN, C::THREADS>(
+      part, full, splits, 1.0f, T, t_slices, t_stride, r, L2, bias, Y, N, 0, M, 0, N, act, lds);
+}
+
+// Remainder split, as for the int4 GEMM: only for the big tile (one workgroup
+// per CU, so a wave of workgroups is `cus` tiles), and only when the last wave
+// is at most a quarter full: then up to 8 K-shares per tile fit in one wave.
+struct MxSplit {
+  int full = 0, rem = 0, splits = 1;
+  size_t part_bytes = 0;
+};
+
+template <class C>
+MxSplit plan_split(int M, int N, int K) {
+  MxSplit p;
+  const int tiles = tiles_of<C>(M, N);
+  const int cus = cu_count_mx();
+  const int ksteps = K / KS;
+  p.full = tiles;
+  const int rem = tiles % cus;
+  if (C::BM * C::BN < MxBig::BM * MxBig::BN || tiles < cus || rem == 0 || 4 * rem > cus) return p;
+  const int splits = std::min(std::min(kMaxSplits, cus / rem), ksteps);
+  if (splits < 2) return p;
+  p.full = tiles - rem;
+  p.rem = rem;
+  p.splits = splits;
+  p.part_bytes = (size_t)rem * splits * C::BM * C::BN * sizeof(float);
+  return p;
+}
+
 template <class C>
 hipError_t launch(const uint8_t* qx, const uint8_t* sx, int sx_rows, const float* T, int t_slices,
                   int M, int K, int N, int r, const uint16_t* L2, const uint8_t* Wq,
-                  const uint8_t* sw, const uint16_t* bias, uint16_t* Y, int act,
+                  const uint8_t* sw, const uint16_t* bias, uint16_t* Y, float* part, int act,
                   hipStream_t stream) {
-  hipLaunchKernelGGL(mxfp4_gemm_kernel<C>, dim3(tiles_of<C>(M, N)), dim3(C::THREADS), 0,
-                     stream, qx, sx, sx_rows, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias,
-                     Y, act);
+  const MxSplit p = plan_split<C>(M, N, K);
+  hipLaunchKernelGGL((mxfp4_gemm_kernel<C, kWhole>), dim3(p.full), dim3(C::THREADS), 0, stream, qx,
+                     sx, sx_rows, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw, bias, Y, act,
+                     p.full, p.rem, p.splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.rem == 0) return e;
+  hipLaunchKernelGGL((mxfp4_gemm_kernel<C, kShares>), dim3(p.rem * p.splits), dim3(C::THREADS), 0,
+                     stream, qx, sx, sx_rows, T, t_slices, (long)M * r, M, K, N, r, L2, Wq, sw,
+                     bias, Y, act, p.full, p.rem, p.splits, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((mxfp4_fixup_kernel<C>), dim3(p.rem * C::WM), dim3(64 * C::TM * C::WN),
+                     16 * C::TM * C::BN * 2, stream, part, p.full, p.splits, T, t_slices,
+                     (long)M * r, r, L2, bias, Y, M, N, act);
   return hipGetLastError();
+}
+
+MxSplit plan_forward(int M, int N, int K) {
+  const int cus = cu_count_mx();
+  if (tiles_of<MxBig>(M, N) >= cus) return plan_split<MxBig>(M, N, K);
+  if (tiles_of<MxMed>(M, N) >= cus) return plan_split<MxMed>(M, N, K);
+  return plan_split<MxSmall>(M, N, K);
 }
 
 }  // namespace
 
+size_t mxfp4_gemm_split_bytes(int M, int K, int N) { return plan_forward(M, N, K).part_bytes; }
+
 hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_rows, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
-                             uint16_t* Y, int act, hipStream_t stream) {
+                             uint16_t* Y, float* part, int act, hipStream_t stream) {
   const int cus = cu_count_mx();
   if (tiles_of<MxBig>(M, N) >= cus)
-    return launch<MxBig>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+    return launch<MxBig>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y,
+                         part, act, stream);
   if (tiles_of<MxMed>(M, N) >= cus)
-    return launch<MxMed>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
-  return launch<MxSmall>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y, act, stream);
+    return launch<MxMed>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y,
+                         part, act, stream);
+  return launch<MxSmall>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y,
+                         part, act, stream);
 }
 
 }  // namespace svdq

@@ -99,24 +99,9 @@ __device__ inline i32x4 as_i32x4(uint4 v) {
   return r;
 }
 
-// Tile coordinates of tile number `id`: rastered in groups of 8 token tiles.
-__device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
-  const int per_group = GROUP_M * ntn;
-  const int grp = id / per_group;
-  const int first = grp * GROUP_M;
-  const int gsize = min(ntm - first, GROUP_M);
-  const int in = id - grp * per_group;
-  tm = first + in % gsize;
-  tn = in / gsize;
-}
-
-// Workgroups are dealt round-robin to the 8 XCDs; block b of `count` (a
-// multiple of 8) gets tile number (b % 8) * count / 8 + b / 8, so that each
-// XCD works on one compact run of tiles and keeps its qx and Wq rows in its L2.
-__device__ inline int xcd_compact(int b, int count) {
-  return (count & 7) == 0 ? (b & 7) * (count >> 3) + (b >> 3) : b;
-}
+using tail::tile_of_id;
+using tail::xcd_compact;
+using tail::kMaxSplits;
 
 // EXPORT = false: the forward.  EXPORT = true: write the group partials P of
 // tokens [row0, row1) x features [col0, col1) instead of the epilogue.
@@ -127,7 +112,6 @@ __device__ inline int xcd_compact(int b, int count) {
 // MODE kShares: block u computes share u / rem of tile full + u % rem and
 // stores its raw fp32 accumulators in `part`.  w4a4_fixup_kernel sums them.
 constexpr int kWhole = 0, kShares = 1;
-constexpr int kMaxSplits = 8;      // K-shares per remainder tile, at most
 
 template <class C, bool EXPORT, int MODE>
 __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
@@ -464,13 +448,8 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
       [&](int row) { return otile + row * C::BN; }, act);
 }
 
-// Fixup of the remainder split.  Block (t, wm) covers the 64-row band wm of
-// remainder tile full + t at the tile's full width: its waves stand in for
-// the band's (16-row slice, wave column) pairs, and each sums its accumulator
-// entries over the shares in split order, all of its loads issued at once.
-// The sums, the 1/256, the low-rank tail and the store are those the tile's
-// own waves would run, element for element.  rem x WM blocks spread over the
-// chip what rem blocks of a whole tile each would otherwise read alone.
+// Fixup of the remainder split (tail::split_fixup): the accumulators are
+// 256 times the scaled sums.
 template <class C>
 __global__ __launch_bounds__(64 * C::TM * C::WN) void w4a4_fixup_kernel(
     const float* __restrict__ part, int full, int splits, const float* __restrict__ T,
@@ -478,58 +457,9 @@ __global__ __launch_bounds__(64 * C::TM * C::WN) void w4a4_fixup_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int ldy, int row0, int row1,
     int col0, int col1, int act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int NACC = C::TM * C::TN;
-  constexpr int BAND = 16 * C::TM;                  // rows of a wave's sub-tile
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int slice = wave % C::TM;                   // the 16-row slice tm of the sub-tile
-  const int wn = wave / C::TM;                      // the wave column it stands in for
-  const int wm = blockIdx.x % C::WM;
-  const int tr = blockIdx.x / C::WM;
-  const int ntm = (row1 - row0 + C::BM - 1) / C::BM;
-  const int ntn = (col1 - col0 + C::BN - 1) / C::BN;
-  int tmi, tni;
-  tile_of_id(ntm, ntn, full + tr, tmi, tni);
-  const int m0 = row0 + tmi * C::BM + wm * BAND;    // the band
-  const int n0 = col0 + tni * C::BN;
-  const int src_tid = (wm * C::WN + wn) * 64 + lane;  // the share writer's thread
-
-  f32x4 acc[1][C::TN];
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) acc[0][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float4* src = reinterpret_cast<const float4*>(part) +
-                      (size_t)tr * splits * NACC * C::THREADS +
-                      (size_t)slice * C::TN * C::THREADS + src_tid;
-  // at most kMaxSplits shares: every load is issued before the first add
-  // (clamped, unconditional); the adds run in split order for the real ones
-  float4 v[kMaxSplits][C::TN];
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
-#pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn)
-      v[sp][tn] = src[((size_t)min(sp, splits - 1) * NACC + tn) * C::THREADS];
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
-    if (sp < splits)
-#pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn) {
-        acc[0][tn][0] += v[sp][tn].x;
-        acc[0][tn][1] += v[sp][tn].y;
-        acc[0][tn][2] += v[sp][tn].z;
-        acc[0][tn][3] += v[sp][tn].w;
-      }
-#pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[0][tn][i] *= (1.0f / 256.0f);
-  const int wr = 16 * slice, wc = wn * C::TN * 16;
-  tail::lowrank_bias_add<1, C::TN, 2>(acc, T, t_slices, t_stride, r, L2, bias, m0, n0, row1, col1,
-                                      wr, wc, lane, 1.0f, [] {});
-  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
-  tail::store_tile<1, C::TN, BAND, C::BN, 64 * C::TM * C::WN>(
-      acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
-      [&](int row) { return otile + row * C::BN; }, act);
+  tail::split_fixup<C::TM, C::TN, C::WM, C::WN, C::BM, C::BN, C::THREADS>(
+      part, full, splits, 1.0f / 256.0f, T, t_slices, t_stride, r, L2, bias, Y, ldy, row0, row1,
+      col0, col1, act, lds);
 }
 
 int cu_count() {

@@ -42,7 +42,7 @@ Workspace carve_workspace(void* base, int M, int K, int N, int r) {
 
 // MXFP4 workspace: qx [M, K/2] | sx k-tiled E8M0 bytes [ceil(K/256)][sx_rows][8]
 // | T [slices, M, r].
-MxWorkspace carve_workspace_mx(void* base, int M, int K, int r) {
+MxWorkspace carve_workspace_mx(void* base, int M, int K, int N, int r) {
   MxWorkspace w;
   uint8_t* p = static_cast<uint8_t*>(base);
   w.sx_rows = (M + 1) & ~1;
@@ -50,10 +50,12 @@ MxWorkspace carve_workspace_mx(void* base, int M, int K, int r) {
   const size_t sx_bytes = align256((size_t)((K + 255) / 256) * w.sx_rows * 8);
   w.t_slices = k1_plan(M, K, r, false).slices;
   const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
+  const size_t part_bytes = N > 0 ? align256(mxfp4_gemm_split_bytes(M, K, N)) : 0;
   w.qx = p;
   w.sx = p + qx_bytes;
   w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
-  w.bytes = qx_bytes + sx_bytes + t_bytes;
+  w.part = part_bytes ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes + t_bytes) : nullptr;
+  w.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
   return w;
 }
 
@@ -176,11 +178,11 @@ svdq_status forward_gemm_mx(int M, int K, int N, int r, const uint16_t* L2, cons
   SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
   SVDQ_TRY(check_act(act));
   SVDQ_TRY(check_ptr(workspace, "workspace", false));
-  const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, r);
+  const MxWorkspace w = carve_workspace_mx(const_cast<void*>(workspace), M, K, N, r);
   if (workspace_bytes < w.bytes)
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
   return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.sx_rows, w.T, w.t_slices, M, K, N, r, L2, Wq,
-                                     w_e8m0, bias, Y, act, static_cast<hipStream_t>(stream)),
+                                     w_e8m0, bias, Y, w.part, act, static_cast<hipStream_t>(stream)),
                    "mxfp4_gemm launch");
 }
 
@@ -193,7 +195,7 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
   SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
   SVDQ_TRY(check_act(act));
   SVDQ_TRY(check_ptr(workspace, "workspace", false));
-  const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
+  const MxWorkspace w = carve_workspace_mx(workspace, M, K, N, r);
   if (workspace_bytes < w.bytes)
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -201,7 +203,7 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
                                                       false, w.sx_rows, s),
                      "smooth_quant_lora_down (MXFP4) launch"));
   return hip_check(launch_mxfp4_gemm(w.qx, w.sx, w.sx_rows, w.T, w.t_slices, M, K, N, r, L2, Wq,
-                                     w_e8m0, bias, Y, act, s),
+                                     w_e8m0, bias, Y, w.part, act, s),
                    "mxfp4_gemm launch");
 }
 
@@ -305,7 +307,7 @@ svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int 
 
 size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r) {
   if (M < 1 || K < 128 || K % 128 || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16) return 0;
-  return carve_workspace_mx(nullptr, M, K, r).bytes;
+  return carve_workspace_mx(nullptr, M, K, N, r).bytes;
 }
 
 svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
@@ -315,7 +317,7 @@ svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
     SVDQ_TRY(check_shapes_mx(M, K, 16, r));
     SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
     SVDQ_TRY(check_ptr(workspace, "workspace", false));
-    const MxWorkspace w = carve_workspace_mx(workspace, M, K, r);
+    const MxWorkspace w = carve_workspace_mx(workspace, M, K, 0, r);   // stage 1 needs no partials
     if (workspace_bytes < w.bytes)
       return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
     return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,

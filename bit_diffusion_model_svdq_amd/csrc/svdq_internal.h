@@ -29,16 +29,21 @@ struct Workspace {
 Workspace carve_workspace(void* base, int M, int K, int N, int r);
 
 // MXFP4 workspace: qx [M, K/2] | sx k-tiled E8M0 bytes [ceil(K/256)][sx_rows][8]
-// | T [slices, M, r].
+// | T [slices, M, r] | split partials (only when the GEMM splits a last
+// partial wave of tiles; N = 0 leaves them out).
 struct MxWorkspace {
   uint8_t* qx;
   uint8_t* sx;
   int sx_rows;      // M rounded up to even: 16-byte runs of two rows stay aligned
   float* T;
   int t_slices;
+  float* part;
   size_t bytes;
 };
-MxWorkspace carve_workspace_mx(void* base, int M, int K, int r);
+MxWorkspace carve_workspace_mx(void* base, int M, int K, int N, int r);
+
+// Bytes of fp32 partial accumulators the MXFP4 GEMM needs for M x N x K.
+size_t mxfp4_gemm_split_bytes(int M, int K, int N);
 
 // Bytes of fp32 partial accumulators k2 needs for an M x N x K forward.
 size_t gemm_split_bytes(int M, int K, int N);
@@ -91,7 +96,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, 
 hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_rows, const float* T,
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
-                             uint16_t* Y, int act, hipStream_t stream);
+                             uint16_t* Y, float* part, int act, hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

@@ -252,6 +252,11 @@ def test_workspace_bytes_mxfp4():
     assert b == al(M * K // 2) + al(M * K // 32) + al(2 * M * r * 4)
     M, K = 77, 640                                                     # odd M, K % 256 == 128
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 48, 0) == al(M * K // 2) + al(3 * 78 * 8)
+    # 4608 tokens, N = 3072: 18 x 16 = 288 tiles of 256 x 192 on 256 CUs leave 32, cut into
+    # 8 K-shares of fp32 partial tiles (a one-slice T at r = 48)
+    M, K, N, r = 4608, 3072, 3072, 48
+    assert S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r) == (
+        al(M * K // 2) + al(M * K // 32) + al(M * r * 4) + al(32 * 8 * 256 * 192 * 4))
     assert S.svdq_forward_workspace_bytes_mxfp4(M, 64, N, r) == 0     # K must be a multiple of 128
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 40, r) == 0
 

@@ -264,3 +264,26 @@ def test_k1_mx_workspace_scales_k_tiled(M, K):
     tiled = w[qbytes:qbytes + nt * rows * 8].reshape(nt, rows, 8)
     got = tiled[:, :M, :].transpose(1, 0, 2).reshape(M, nt * 8)[:, :nb]
     np.testing.assert_array_equal(got, sx_o)
+
+
+def test_forward_mx_remainder_split_ragged():
+    """4300 x 640 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192 on 256 CUs leave 16
+    (including the ragged last token tile) that are cut along K into as many shares as
+    there are 128-channel steps (5), then summed by the fixup pass, which adds the
+    low-rank branch and the bias."""
+    say("forward mx remainder split 4300x640x3072 r=48")
+    M, K, N, r = 4300, 640, 3072, 48
+    w = synth.WORKLOADS["dit_proj"]
+    X = np.ascontiguousarray(synth.activations(w, M)[:, :K])
+    W = np.ascontiguousarray(synth.weight(w)[:N, :K])
+    b = synth.bias(w)[:N]
+    A = O.act_absmax(synth.calibration_activations(w)[:, :K])
+    pk = O.pack_weights(W, A, 0.5, rank=r)
+    Wq, we = O.quantize_residual_mx(W, pk["s"], pk["L1"], pk["L2"])
+    p = dict(X=X, b=b, M=M, K=K, N=N, r=r, s=pk["s"], L1=pk["L1"], L2=pk["L2"], Wq=Wq, we=we,
+             we_tiled=S.svdq_mxfp4_tile_scales(we))
+    Yg = run_forward(p)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(4090, 4110), np.arange(M - 40, M),
+                                     synth.rng_for("dit_proj", 34).choice(M, 200, replace=False)]))
+    Yref = O.forward_mx(X[rows], pk["s"], pk["L1"], pk["L2"], Wq, we, b)
+    check_y(Yg[rows], Yref, "mx remainder split")

@@ -284,9 +284,10 @@ def test_forward_with_appended_lora_r48():
 
 
 def test_forward_remainder_split_ragged():
-    """4300 x 256 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192, so 16 tiles
-    (including the ragged last token tile) are cut along K into as many shares as
-    there are stages (2) and summed by the fixup pass."""
+    """4300 x 256 -> 3072, r = 48: 256 x 192 tiles (17 x 16 = 272) would leave a partial
+    wave, so 128 x 192 tiles run two per CU: 34 x 16 = 544 leave 32 tiles (including the
+    ragged last token tile) that are cut along K into as many shares as there are stages
+    (2) and summed by the fixup pass."""
     say("forward remainder split 4300x256x3072 r=48")
     w = synth.WORKLOADS["dit_proj"]
     M, K, N, r = 4300, 256, 3072, 48
