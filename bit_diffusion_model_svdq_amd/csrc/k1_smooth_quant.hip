@@ -471,9 +471,10 @@ hipError_t dispatch(const uint16_t* X, int M, int K, int r, const float* smooth,
 // Row tiles per workgroup (RTM = 1 or 2) and K-slices, from a cost model in
 // rough microseconds, fitted to measured launches on MI355X:
 //   rounds * (5 + 2 * groups_per_wave * w)          waves of workgroups over 256 CUs
-//   + 10 * (256 - workgroups) / 256 when under 256   idle CUs
-//   + 4 per T slice beyond the first                  the GEMM re-reads every slice of
+//   + 20 * (256 - workgroups) / 256 when under 256   idle CUs
+//   + 6 per T slice beyond the first                  the GEMM re-reads every slice of
 //                                                    T for each of its output tiles
+//                                                    (the MXFP4 GEMM in its prologue)
 // where w = 1 + 0.5 r / (16 RTM) weighs a group's X bytes with the L1
 // fragments it needs (read from L2 once per 16 RTM rows).  A wave waits one
 // memory round trip per group, so fewer groups per wave shorten a workgroup;
@@ -505,7 +506,7 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice) {
       const long n = (long)rb * slices;
       const long rounds = (n + kCus - 1) / kCus;
       const double cost = rounds * (5.0 + 2.0 * per_wave * w) +
-                          (n < kCus ? 10.0 * (kCus - n) / kCus : 0.0) + 4.0 * (slices - 1);
+                          (n < kCus ? 20.0 * (kCus - n) / kCus : 0.0) + 6.0 * (slices - 1);
       if (cost < best - 1e-9) {
         best = cost;
         p.rtm = rtm;
