@@ -34,8 +34,9 @@
 //
 // The low-rank branch's up projection T L2^T initializes the accumulators
 // before the main loop (its loads are issued together, without branches, right
-// after the first stage's copies), so that only the bias and the store are
-// left after it.
+// after the first NR - 1 steps' copies), so that only the bias and the store
+// are left after it.  A nearly empty last wave of tiles is cut along K into
+// shares finished by tail::split_fixup, which adds the branch there instead.
 #include "gemm_tail.h"
 #include "svdq_internal.h"
 
