@@ -7,6 +7,8 @@
 // of the tile through LDS as 16-byte row segments.
 #pragma once
 
+#include <type_traits>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -182,21 +184,29 @@ __device__ inline void store_tile(f32x4 (&acc)[TM][TN], const uint16_t* __restri
                   : 0.f;
 
   // columns swizzled by 16 elements per group of 4 rows, so that the 4 row
-  // groups of a write hit distinct banks
+  // groups of a write hit distinct banks.  The activation is a compile-time
+  // choice inside the loops: a run-time test there is if-converted, and the
+  // GELU's exp and reciprocal would then run for every element either way.
+  auto write = [&](auto gelu) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wr + 16 * tm + 4 * fk + i;
-      uint16_t* orow = row_lds(row);
+      for (int i = 0; i < 4; ++i) {
+        const int row = wr + 16 * tm + 4 * fk + i;
+        uint16_t* orow = row_lds(row);
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int col = wc + 16 * tn + fr;
-        float v = acc[tm][tn][i] + bv[tn];
-        if (act == kActGeluTanh) v = gelu_tanh(v);
-        orow[col ^ (16 * ((row >> 2) & 3))] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        for (int tn = 0; tn < TN; ++tn) {
+          const int col = wc + 16 * tn + fr;
+          float v = acc[tm][tn][i] + bv[tn];
+          if constexpr (decltype(gelu)::value) v = gelu_tanh(v);
+          orow[col ^ (16 * ((row >> 2) & 3))] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
       }
-    }
+  };
+  if (act == kActGeluTanh)
+    write(std::true_type{});
+  else
+    write(std::false_type{});
   __syncthreads();
   constexpr int CPR = BN / 8;   // 16-byte chunks per output row
   for (int c = tid; c < BM * CPR; c += THREADS) {
