@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -63,9 +64,23 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "bit_diffusion_model_svdq_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(name: str, root: str = ROOT) -> str:
+    """sha256 over a kernel source and every local header it includes (transitively)."""
+    dirs = [os.path.join(root, "bit_diffusion_model_svdq_amd", "csrc"), os.path.join(root, "include")]
+    h = hashlib.sha256()
+    seen, todo = set(), [name]
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.add(f)
+        path = next((os.path.join(d, f) for d in dirs if os.path.exists(os.path.join(d, f))), None)
+        if path is None:
+            raise FileNotFoundError(f)
+        text = open(path, "rb").read()
+        h.update(f.encode() + b"\0" + text)
+        todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', text.decode(), flags=re.M)
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_file: str, workload: str):
