@@ -329,13 +329,22 @@ __global__ __launch_bounds__(64 * C::TM * C::WN) void mxfp4_fixup_kernel(
       part, full, splits, 1.0f, T, t_slices, t_stride, r, L2, bias, Y, N, 0, M, 0, N, act, lds);
 }
 
-// Remainder split, as for the int4 GEMM: only for the big tile (one workgroup
-// per CU, so a wave of workgroups is `cus` tiles), and only when the last wave
-// is at most a quarter full: then up to 8 K-shares per tile fit in one wave.
+// Remainder split, as for the int4 GEMM: only for tiles that fill a CU (a wave
+// of workgroups is `cus * WPE` tiles), only when the last wave is at most a
+// quarter full (then up to 8 K-shares per tile fit in one wave), and only for
+// K of at least kMinSplitSteps steps.
 struct MxSplit {
   int full = 0, rem = 0, splits = 1;
   size_t part_bytes = 0;
 };
+
+// The remainder split pays only where a share still runs enough steps to
+// cover the round trip of its fp32 partials and the fixup pass.  Measured
+// with a 4608 x K -> 3072 GEMM (rem = 32 of 288 tiles): at K = 4608 and 6144
+// (36 and 48 steps) the 128 x 192 tile without a split was 8 and 3.5 us
+// faster than 8 shares; at K = 8192 (64 steps) the split was 4 us faster; at
+// K = 12288 20 us.
+constexpr int kMinSplitSteps = 56;
 
 template <class C>
 MxSplit plan_split(int M, int N, int K) {
@@ -345,7 +354,8 @@ MxSplit plan_split(int M, int N, int K) {
   const int ksteps = K / KS;
   p.full = tiles;
   const int rem = tiles % cus;
-  if (C::BM * C::BN * C::WPE < MxBig::BM * MxBig::BN || tiles < cus || rem == 0 || 4 * rem > cus)
+  if (C::BM * C::BN * C::WPE < MxBig::BM * MxBig::BN || tiles < cus || rem == 0 || 4 * rem > cus ||
+      ksteps < kMinSplitSteps)
     return p;
   const int splits = std::min(std::min(kMaxSplits, cus / rem), ksteps);
   if (splits < 2) return p;
@@ -379,24 +389,26 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, int sx_rows, const float
 
 // Tile choice: the biggest tile that still gives every CU at least one
 // workgroup.  256 x 192 tiles are kept where they fill whole waves or leave a
-// last wave at most a quarter full (which the remainder split finishes);
-// between those, the 128 x 192 tile with two workgroups per CU takes over:
+// last wave at most a quarter full that the remainder split finishes (K of at
+// least kMinSplitSteps steps); otherwise the 128 x 192 tile with two
+// workgroups per CU takes over (at K = 3072 with 32 remainder tiles: 52 us
+// against 66 us with the split):
 // finer granularity, and one workgroup's waits run under the other's MFMAs
 // (measured 9-10 % faster on the 4608-token QKV and up projections, 12 %
 // slower than the split on the down projection).
-int pick_tile(int M, int N) {
+int pick_tile(int M, int N, int K) {
   const int cus = cu_count_mx();
   const int big = tiles_of<MxBig>(M, N);
   if (big >= cus) {
     const int rem = big % cus;
-    return rem == 0 || 4 * rem <= cus ? 2 : 3;
+    return rem == 0 || (4 * rem <= cus && K / KS >= kMinSplitSteps) ? 2 : 3;
   }
   if (tiles_of<MxMed>(M, N) >= cus) return 1;
   return 0;
 }
 
 MxSplit plan_forward(int M, int N, int K) {
-  switch (pick_tile(M, N)) {
+  switch (pick_tile(M, N, K)) {
     case 3: return plan_split<MxBig2>(M, N, K);
     case 2: return plan_split<MxBig>(M, N, K);
     case 1: return plan_split<MxMed>(M, N, K);
@@ -412,7 +424,7 @@ hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_r
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
                              uint16_t* Y, float* part, int act, hipStream_t stream) {
-  switch (pick_tile(M, N)) {
+  switch (pick_tile(M, N, K)) {
     case 3:
       return launch<MxBig2>(qx, sx_e8m0, sx_rows, T, t_slices, M, K, N, r, L2, Wq, w_e8m0, bias, Y,
                             part, act, stream);

@@ -252,11 +252,22 @@ def test_workspace_bytes_mxfp4():
     assert b == al(M * K // 2) + al(M * K // 32) + al(2 * M * r * 4)
     M, K = 77, 640                                                     # odd M, K % 256 == 128
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 48, 0) == al(M * K // 2) + al(3 * 78 * 8)
-    # 4608 tokens, N = 3072: 18 x 16 = 288 tiles of 256 x 192 on 256 CUs leave 32, cut into
-    # 8 K-shares of fp32 partial tiles (a one-slice T at r = 48)
+    # 4608 tokens, N = 3072: 18 x 16 = 288 tiles of 256 x 192 on 256 CUs leave 32.  At
+    # K = 3072 (24 steps) they are too short to split: no partials (a one-slice T at r = 48)
     M, K, N, r = 4608, 3072, 3072, 48
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r) == (
-        al(M * K // 2) + al(M * K // 32) + al(M * r * 4) + al(32 * 8 * 256 * 192 * 4))
+        al(M * K // 2) + al(M * K // 32) + al(M * r * 4))
+    # at K = 12288 (96 steps) the 32 are cut into 8 K-shares of fp32 partial tiles; k1 runs
+    # 5 K-slices of 39 groups, so T has 5 slices
+    K = 12288
+    assert S.svdq_forward_workspace_bytes_mxfp4(M, K, N, r) == (
+        al(M * K // 2) + al(M * K // 32) + al(5 * M * r * 4) + al(32 * 8 * 256 * 192 * 4))
+    # the threshold: 56 steps split, 55 do not
+    part = al(16 * 8 * 256 * 192 * 4)
+    for K, split in ((7168, True), (7040, False)):
+        base = S.svdq_forward_workspace_bytes_mxfp4(4300, K, N, 0)
+        assert base == al(4300 * K // 2) + al((K + 255) // 256 * 4300 * 8) + (part if split else 0), K
+    K = 3072
     assert S.svdq_forward_workspace_bytes_mxfp4(M, 64, N, r) == 0     # K must be a multiple of 128
     assert S.svdq_forward_workspace_bytes_mxfp4(M, K, 40, r) == 0
 

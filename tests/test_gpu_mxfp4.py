@@ -266,14 +266,8 @@ def test_k1_mx_workspace_scales_k_tiled(M, K):
     np.testing.assert_array_equal(got, sx_o)
 
 
-def test_forward_mx_remainder_split_ragged():
-    """4300 x 640 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192 on 256 CUs leave 16
-    (including the ragged last token tile) that are cut along K into as many shares as
-    there are 128-channel steps (5), then summed by the fixup pass, which adds the
-    low-rank branch and the bias."""
-    say("forward mx remainder split 4300x640x3072 r=48")
-    M, K, N, r = 4300, 640, 3072, 48
-    w = synth.WORKLOADS["dit_proj"]
+def _mx_ragged_case(M, K, N, r, wname, tag):
+    w = synth.WORKLOADS[wname]
     X = np.ascontiguousarray(synth.activations(w, M)[:, :K])
     W = np.ascontiguousarray(synth.weight(w)[:N, :K])
     b = synth.bias(w)[:N]
@@ -286,4 +280,22 @@ def test_forward_mx_remainder_split_ragged():
     rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(4090, 4110), np.arange(M - 40, M),
                                      synth.rng_for("dit_proj", 34).choice(M, 200, replace=False)]))
     Yref = O.forward_mx(X[rows], pk["s"], pk["L1"], pk["L2"], Wq, we, b)
-    check_y(Yg[rows], Yref, "mx remainder split")
+    check_y(Yg[rows], Yref, tag)
+
+
+def test_forward_mx_partial_wave_ragged():
+    """4300 x 640 -> 3072, r = 48: 17 x 16 = 272 tiles of 256 x 192 on 256 CUs leave 16.
+    With 5 steps of 128 channels, K is too short for the remainder split, so 128 x 192
+    tiles at two workgroups per CU run the GEMM: 544 tiles, the last wave partly
+    filled, the last token tile ragged."""
+    say("forward mx partial wave 4300x640x3072 r=48")
+    _mx_ragged_case(4300, 640, 3072, 48, "dit_proj", "mx partial wave")
+
+
+def test_forward_mx_remainder_split_ragged():
+    """4300 x 7168 -> 3072, r = 48: 272 tiles of 256 x 192 on 256 CUs leave 16
+    (including the ragged last token tile). With 56 steps of 128 channels, each is cut
+    along K into 8 shares, which the fixup pass sums before it adds the low-rank
+    branch and the bias."""
+    say("forward mx remainder split 4300x7168x3072 r=48")
+    _mx_ragged_case(4300, 7168, 3072, 48, "mlp_down", "mx remainder split")
