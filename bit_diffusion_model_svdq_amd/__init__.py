@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+# SVDQ_LIBRARY names another build of the same library (the host-sanitizer build
+# that the CPU tests can run against); by default the in-tree libsvdq.so.
+LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(_HERE, "libsvdq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with python bit_diffusion_model_svdq_amd/build.py")
@@ -47,6 +49,8 @@ EXPORTS = [
     "svdq_forward_quantize_mxfp4", "svdq_forward_gemm_mxfp4", "svdq_quantize_activations_mxfp4",
     "svdq_linear_forward_act", "svdq_forward_gemm_act", "svdq_linear_forward_act_mxfp4",
     "svdq_forward_gemm_act_mxfp4", "svdq_mxfp4_tiled_scale_bytes", "svdq_mxfp4_tile_scales",
+    "svdq_act_absmax_update_device", "svdq_forward_workspace_layout",
+    "svdq_forward_workspace_layout_mxfp4",
 ]
 
 # svdq_activation
@@ -79,6 +83,9 @@ _sig = {
     "svdq_forward_gemm": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "svdq_quantize_activations": [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P],
     "svdq_debug_group_partials": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
+    "svdq_act_absmax_update_device": [_P, ctypes.c_int64, _I, _P, _P],
+    "svdq_forward_workspace_layout": [_I, _I, _I, _I, _P, _P, _P, _P],
+    "svdq_forward_workspace_layout_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P],
     "svdq_quantize_residual_mxfp4": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_bytes_mxfp4": [_I, _I, _I, _I],
     "svdq_linear_forward_mxfp4": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -193,6 +200,70 @@ def _dp(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# The C ABI sees only pointers, so a wrong tensor would be read or written out
+# of bounds; every device wrapper checks its tensors against the shapes the
+# library will assume before it calls in.
+_BF16 = ("int16", "bfloat16")      # bf16 bit patterns: int16 views or torch.bfloat16
+
+
+def _need(t, name, dtypes, shape=None, numel=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} must not be None")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_contiguous"):
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    dt = str(t.dtype).replace("torch.", "")
+    if dtypes is not None and dt not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(dtypes)} (got {dt})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements (got {t.numel()})")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors live on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _rank_of(L1, L2=None, N=None):
+    r = L1.shape[0] if L1 is not None else 0
+    if (L2 is None) != (L1 is None) and r > 0:
+        raise ValueError("L1 and L2 must both be given (or both None for r = 0)")
+    return r
+
+
+def _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y, mx=False):
+    """Shapes of one layer's device tensors, as include/svdq.h lays them out."""
+    if X is not None:
+        _need(X, "X", _BF16, (M, K))
+    if smooth is not None or X is not None:
+        _need(smooth, "smooth", ("float32",), (K,))
+    if L1 is not None or (X is not None and r > 0):
+        _need(L1, "L1", _BF16, (r, K), optional=r == 0)
+    if Wq is not None:
+        _need(L2, "L2", _BF16, (N, r), optional=r == 0)
+        _need(Wq, "Wq", ("uint8",), (N, K // 2))
+        if mx:
+            _need(w_scales, "w_e8m0", ("uint8",), numel=svdq_mxfp4_tiled_scale_bytes(N, K))
+        else:
+            _need(w_scales, "w_scales", ("float32",), (N, K // 64))
+        _need(bias, "bias", _BF16, (N,), optional=True)
+        _need(Y, "Y", _BF16, (M, N))
+    _same_device(X, smooth, L1, L2, Wq, w_scales, bias, Y)
+
+
+def _check_ws(workspace, *others):
+    _need(workspace, "workspace", None)
+    _same_device(workspace, *others)
+
+
 def _stream(stream=None):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -203,11 +274,31 @@ def svdq_forward_workspace_bytes(M: int, K: int, N: int, r: int) -> int:
     return int(_lib.svdq_forward_workspace_bytes(M, K, N, r))
 
 
+def svdq_forward_workspace_layout(M: int, K: int, N: int, r: int, mxfp4: bool = False) -> dict:
+    """Byte offsets of qx, sx and the T slices inside the forward's workspace, the
+    number of T slices and (MXFP4) the row count of the k-tiled activation scales."""
+    qo, so, to = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    ts, rows = ctypes.c_int(), ctypes.c_int()
+    if mxfp4:
+        st = _lib.svdq_forward_workspace_layout_mxfp4(M, K, N, r, ctypes.byref(qo), ctypes.byref(so),
+                                                      ctypes.byref(to), ctypes.byref(ts), ctypes.byref(rows))
+    else:
+        st = _lib.svdq_forward_workspace_layout(M, K, N, r, ctypes.byref(qo), ctypes.byref(so),
+                                                ctypes.byref(to), ctypes.byref(ts))
+    _check(st, "svdq_forward_workspace_layout")
+    out = dict(qx=qo.value, sx=so.value, T=to.value, t_slices=ts.value)
+    if mxfp4:
+        out["sx_rows"] = rows.value
+    return out
+
+
 def svdq_linear_forward(X, smooth, L1, L2, Wq, w_scales, bias, Y, workspace, stream=None):
     """Y [M, N] (bf16 tensor, written) = SVDQuant linear of X [M, K] bf16.  All tensors on the GPU."""
     M, K = X.shape
     N = Wq.shape[0]
-    r = L1.shape[0] if L1 is not None else 0
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y)
+    _check_ws(workspace, X)
     st = _lib.svdq_linear_forward(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
                                   _dp(w_scales), _dp(bias), _dp(Y), _dp(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
@@ -220,7 +311,9 @@ def svdq_linear_forward_act(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y
     """svdq_linear_forward with an svdq_activation applied to Y (SVDQ_ACT_GELU_TANH: GELU, tanh form)."""
     M, K = X.shape
     N = Wq.shape[0]
-    r = L1.shape[0] if L1 is not None else 0
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y)
+    _check_ws(workspace, X)
     st = _lib.svdq_linear_forward_act(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
                                       _dp(w_scales), _dp(bias), int(activation), _dp(Y), _dp(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
@@ -231,6 +324,8 @@ def svdq_linear_forward_act(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y
 def svdq_forward_quantize(X, smooth, L1, workspace, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
+    _check_layer(X, M, K, 16, r, smooth, L1, None, None, None, None, None)
+    _check_ws(workspace, X)
     st = _lib.svdq_forward_quantize(_dp(X), M, K, r, _dp(smooth), _dp(L1), _dp(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "svdq_forward_quantize")
@@ -238,6 +333,8 @@ def svdq_forward_quantize(X, smooth, L1, workspace, stream=None):
 
 def svdq_forward_gemm(M, K, L2, Wq, w_scales, bias, Y, workspace, r, stream=None):
     N = Wq.shape[0]
+    _check_layer(None, M, K, N, r, None, None, L2, Wq, w_scales, bias, Y)
+    _check_ws(workspace, Wq)
     st = _lib.svdq_forward_gemm(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_scales), _dp(bias), _dp(Y),
                                 _dp(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream))
@@ -246,6 +343,8 @@ def svdq_forward_gemm(M, K, L2, Wq, w_scales, bias, Y, workspace, r, stream=None
 
 def svdq_forward_gemm_act(M, K, L2, Wq, w_scales, bias, activation, Y, workspace, r, stream=None):
     N = Wq.shape[0]
+    _check_layer(None, M, K, N, r, None, None, L2, Wq, w_scales, bias, Y)
+    _check_ws(workspace, Wq)
     st = _lib.svdq_forward_gemm_act(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_scales), _dp(bias),
                                     int(activation), _dp(Y), _dp(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
@@ -255,15 +354,40 @@ def svdq_forward_gemm_act(M, K, L2, Wq, w_scales, bias, activation, Y, workspace
 def svdq_quantize_activations(X, smooth, L1, qx, sx, T, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
+    _check_layer(X, M, K, 16, r, smooth, L1, None, None, None, None, None)
+    _need(qx, "qx", ("uint8",), (M, K // 2))
+    _need(sx, "sx", ("float32",), (M, K // 64))
+    _need(T, "T", ("float32",), (M, r), optional=r == 0)
+    _same_device(X, qx, sx, T)
     st = _lib.svdq_quantize_activations(_dp(X), M, K, _dp(smooth), _dp(L1), r, _dp(qx), _dp(sx),
                                         _dp(T), _stream(stream))
     _check(st, "svdq_quantize_activations")
+
+
+def svdq_act_absmax_update_device(X, amax, stream=None):
+    """Folds bf16 rows X [M, K] (GPU tensor) into the running abs-max amax [K]
+    (float32 GPU tensor holding values >= +0, updated in place)."""
+    if X.dim() != 2:
+        raise ValueError("X must be a [M, K] tensor")
+    M, K = X.shape
+    _need(X, "X", _BF16, (M, K))
+    _need(amax, "amax", ("float32",), (K,))
+    _same_device(X, amax)
+    st = _lib.svdq_act_absmax_update_device(_dp(X), M, K, _dp(amax), _stream(stream))
+    _check(st, "svdq_act_absmax_update_device")
+    return amax
 
 
 def svdq_debug_group_partials(qx, Wq, m0, m1, n0, n1, P, stream=None):
     M = qx.shape[0]
     K = qx.shape[1] * 2
     N = Wq.shape[0]
+    _need(qx, "qx", ("uint8",), (M, K // 2))
+    _need(Wq, "Wq", ("uint8",), (N, K // 2))
+    if not (0 <= m0 < m1 <= M and 0 <= n0 < n1 <= N):
+        raise ValueError(f"block [{m0},{m1})x[{n0},{n1}) is outside [0,{M})x[0,{N})")
+    _need(P, "P", ("int32",), (m1 - m0, n1 - n0, K // 64))
+    _same_device(qx, Wq, P)
     st = _lib.svdq_debug_group_partials(_dp(qx), _dp(Wq), M, N, K, m0, m1, n0, n1, _dp(P),
                                         _stream(stream))
     _check(st, "svdq_debug_group_partials")
@@ -316,7 +440,9 @@ def svdq_forward_workspace_bytes_mxfp4(M: int, K: int, N: int, r: int) -> int:
 def svdq_linear_forward_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, Y, workspace, stream=None):
     M, K = X.shape
     N = Wq.shape[0]
-    r = L1.shape[0] if L1 is not None else 0
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y, mx=True)
+    _check_ws(workspace, X)
     st = _lib.svdq_linear_forward_mxfp4(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
                                         _dp(w_e8m0), _dp(bias), _dp(Y), _dp(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream))
@@ -328,7 +454,9 @@ def svdq_linear_forward_act_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, activatio
                                   stream=None):
     M, K = X.shape
     N = Wq.shape[0]
-    r = L1.shape[0] if L1 is not None else 0
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y, mx=True)
+    _check_ws(workspace, X)
     st = _lib.svdq_linear_forward_act_mxfp4(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2),
                                             _dp(Wq), _dp(w_e8m0), _dp(bias), int(activation), _dp(Y),
                                             _dp(workspace), workspace.numel() * workspace.element_size(),
@@ -340,6 +468,8 @@ def svdq_linear_forward_act_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, activatio
 def svdq_forward_quantize_mxfp4(X, smooth, L1, workspace, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
+    _check_layer(X, M, K, 16, r, smooth, L1, None, None, None, None, None)
+    _check_ws(workspace, X)
     st = _lib.svdq_forward_quantize_mxfp4(_dp(X), M, K, r, _dp(smooth), _dp(L1), _dp(workspace),
                                           workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "svdq_forward_quantize_mxfp4")
@@ -347,6 +477,8 @@ def svdq_forward_quantize_mxfp4(X, smooth, L1, workspace, stream=None):
 
 def svdq_forward_gemm_mxfp4(M, K, L2, Wq, w_e8m0, bias, Y, workspace, r, stream=None):
     N = Wq.shape[0]
+    _check_layer(None, M, K, N, r, None, None, L2, Wq, w_e8m0, bias, Y, mx=True)
+    _check_ws(workspace, Wq)
     st = _lib.svdq_forward_gemm_mxfp4(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_e8m0), _dp(bias), _dp(Y),
                                       _dp(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream))
@@ -356,6 +488,8 @@ def svdq_forward_gemm_mxfp4(M, K, L2, Wq, w_e8m0, bias, Y, workspace, r, stream=
 def svdq_forward_gemm_act_mxfp4(M, K, L2, Wq, w_e8m0, bias, activation, Y, workspace, r,
                                 stream=None):
     N = Wq.shape[0]
+    _check_layer(None, M, K, N, r, None, None, L2, Wq, w_e8m0, bias, Y, mx=True)
+    _check_ws(workspace, Wq)
     st = _lib.svdq_forward_gemm_act_mxfp4(M, K, N, r, _dp(L2), _dp(Wq), _dp(w_e8m0), _dp(bias),
                                           int(activation), _dp(Y), _dp(workspace),
                                           workspace.numel() * workspace.element_size(), _stream(stream))
@@ -365,6 +499,11 @@ def svdq_forward_gemm_act_mxfp4(M, K, L2, Wq, w_e8m0, bias, activation, Y, works
 def svdq_quantize_activations_mxfp4(X, smooth, L1, qx, sx_e8m0, T, stream=None):
     M, K = X.shape
     r = L1.shape[0] if L1 is not None else 0
+    _check_layer(X, M, K, 16, r, smooth, L1, None, None, None, None, None)
+    _need(qx, "qx", ("uint8",), (M, K // 2))
+    _need(sx_e8m0, "sx_e8m0", ("uint8",), (M, K // 32))
+    _need(T, "T", ("float32",), (M, r), optional=r == 0)
+    _same_device(X, qx, sx_e8m0, T)
     st = _lib.svdq_quantize_activations_mxfp4(_dp(X), M, K, _dp(smooth), _dp(L1), r, _dp(qx),
                                               _dp(sx_e8m0), _dp(T), _stream(stream))
     _check(st, "svdq_quantize_activations_mxfp4")

@@ -255,8 +255,10 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
       amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, __shfl_xor(amax, 32));
-      scale = __float_as_uint(amax / 7.0f);
-      const float inv = amax > 0.f ? 7.0f / amax : 0.f;
+      // a group below 2^-100 (zero included) is a zero group: scale 0, codes 0
+      const bool coded = amax >= 0x1p-100f;
+      scale = coded ? __float_as_uint(amax / 7.0f) : 0u;
+      const float inv = coded ? 7.0f / amax : 0.f;
       float z[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
@@ -516,6 +518,12 @@ K1Plan k1_plan(int M, int K, int r, bool one_slice) {
     }
   }
   return p;
+}
+
+// The launch plans keep to kLdsBudget; a one-slice launch may use all of the
+// 160 KB a workgroup can hold.
+bool k1_one_slice_fits(int K, int r) {
+  return lds_bytes(1, K / kGroup, r) <= 160 * 1024;
 }
 
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,

@@ -103,8 +103,10 @@ using tail::tile_of_id;
 using tail::xcd_compact;
 using tail::kMaxSplits;
 
-// EXPORT = false: the forward.  EXPORT = true: write the group partials P of
-// tokens [row0, row1) x features [col0, col1) instead of the epilogue.
+// EXPORT = false: the forward.  EXPORT = true: the forward's own launch (the
+// same tiles and the same remainder shares) writes the group partials P of the
+// window tokens [e_m0, e_m1) x features [e_n0, e_n1) instead of running the
+// epilogue.
 //
 // Remainder split.  When the tile count leaves a last, nearly empty wave of
 // workgroups, tile numbers [full, full + rem) are cut along K into `splits`
@@ -119,8 +121,8 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
     int K, int r, const uint16_t* __restrict__ L2, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scales, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ Y, int ldy, int row0, int row1, int col0, int col1,
-    int32_t* __restrict__ P, int full, int rem, int splits, float* __restrict__ part,
-    int t_slices, long t_stride, int act) {
+    int32_t* __restrict__ P, int e_m0, int e_m1, int e_n0, int e_n1, int full, int rem,
+    int splits, float* __restrict__ part, int t_slices, long t_stride, int act) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,27 +276,32 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
     if (!EXPORT) swc = pswn[0];
     i32x4 dprev[C::TM];
     float2 swp = swc;
-    auto epilogue = [&](const i32x4* d, float2 sw, int tn) {
+    // The scale epilogue of one 16x16 tile (tn, tm): 8 FMAs (EXPORT: the
+    // partials are written instead).
+    auto epilogue_tile = [&](const i32x4& d, float2 sw, int tn, int tm) {
+      if (EXPORT) {
+        const int n = n0 + wc + 16 * tn + fr;
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm) {
-        if (EXPORT) {
-          const int n = n0 + wc + 16 * tn + fr;
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wr + 16 * tm + 4 * fk + i;
+          if (m >= e_m0 && m < e_m1 && n >= e_n0 && n < e_n1)
+            P[((size_t)(m - e_m0) * (e_n1 - e_n0) + (n - e_n0)) * G + gglob] =
+                (d[i] - kMagicBits) >> 8;
+        }
+      } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wr + 16 * tm + 4 * fk + i;
-            if (m < row1 && n < col1)
-              P[((size_t)(m - row0) * (col1 - col0) + (n - col0)) * G + gglob] =
-                  (d[tm][i] - kMagicBits) >> 8;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float t = __builtin_fmaf(__int_as_float(d[tm][i]), sw.x, sw.y);
-            acc[tm][tn][i] = __builtin_fmaf(t, sxv[tm][i], acc[tm][tn][i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const float t = __builtin_fmaf(__int_as_float(d[i]), sw.x, sw.y);
+          acc[tm][tn][i] = __builtin_fmaf(t, sxv[tm][i], acc[tm][tn][i]);
         }
       }
     };
+    // Issue order.  Left alone, the compiler issues all TM x TN MFMAs of the
+    // group before any epilogue; the two waves of a SIMD, kept in step by the
+    // stage barrier, then contend for the matrix core and the VALU in turn.
+    // Instead every MFMA of feature tile tn is paired with the 8 epilogue FMAs
+    // of tile tn - 1 (whose MFMA left TM pairs earlier), each pair fenced off,
+    // so one wave keeps the matrix core and the VALU busy together.
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       i32x4 wnext = wcur;
@@ -305,16 +312,19 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
       }
       i32x4 dcur[C::TM];
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm)
+      for (int tm = 0; tm < C::TM; ++tm) {
         dcur[tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[tm], wcur, cmagic, 0, 0, 0);
-      if (tn > 0) epilogue(dprev, swp, tn - 1);
+        if (tn > 0) epilogue_tile(dprev[tm], swp, tn - 1, tm);
+        if (!EXPORT) __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm) dprev[tm] = dcur[tm];
       swp = swc;
       wcur = wnext;
       swc = swn;
     }
-    epilogue(dprev, swp, C::TN - 1);
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) epilogue_tile(dprev[tm], swp, C::TN - 1, tm);
   };
 
   auto compute_stage = [&](int s, int buf) {
@@ -549,24 +559,25 @@ template <class C, bool EXPORT>
 hipError_t launch_tile(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                        const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                        const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                       int col1, int32_t* P, float* part, int act, hipStream_t stream) {
+                       int col1, int32_t* P, const int* ewin, float* part, int act,
+                       hipStream_t stream) {
   hipError_t e = set_lds_attr<C, EXPORT, kWhole>();
   if (e != hipSuccess) return e;
-  SplitPlan plan;
-  plan.full = tiles_of<C>(row1 - row0, col1 - col0);
-  if (!EXPORT) plan = plan_split<C>(row1 - row0, col1 - col0, K);
+  const SplitPlan plan = plan_split<C>(row1 - row0, col1 - col0, K);
+  const int em0 = EXPORT ? ewin[0] : 0, em1 = EXPORT ? ewin[1] : 0;
+  const int en0 = EXPORT ? ewin[2] : 0, en1 = EXPORT ? ewin[3] : 0;
   hipLaunchKernelGGL((w4a4_gemm_kernel<C, EXPORT, kWhole>), dim3(plan.full), dim3(C::THREADS),
                      C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y, ldy, row0, row1,
-                     col0, col1, P, plan.full, plan.rem, plan.splits, part, t_slices,
-                     (long)(row1 - row0) * r, act);
-  e = hipGetLastError();
-  if (EXPORT || e != hipSuccess || plan.rem == 0) return e;
-  if ((e = set_lds_attr<C, false, kShares>()) != hipSuccess) return e;
-  hipLaunchKernelGGL((w4a4_gemm_kernel<C, false, kShares>), dim3(plan.rem * plan.splits),
-                     dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
-                     ldy, row0, row1, col0, col1, P, plan.full, plan.rem, plan.splits, part,
+                     col0, col1, P, em0, em1, en0, en1, plan.full, plan.rem, plan.splits, part,
                      t_slices, (long)(row1 - row0) * r, act);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = hipGetLastError();
+  if (e != hipSuccess || plan.rem == 0) return e;
+  if ((e = set_lds_attr<C, EXPORT, kShares>()) != hipSuccess) return e;
+  hipLaunchKernelGGL((w4a4_gemm_kernel<C, EXPORT, kShares>), dim3(plan.rem * plan.splits),
+                     dim3(C::THREADS), C::LDS, stream, qx, sx, T, K, r, L2, Wq, w_scales, bias, Y,
+                     ldy, row0, row1, col0, col1, P, em0, em1, en0, en1, plan.full, plan.rem,
+                     plan.splits, part, t_slices, (long)(row1 - row0) * r, act);
+  if ((e = hipGetLastError()) != hipSuccess || EXPORT) return e;
   hipLaunchKernelGGL((w4a4_fixup_kernel<C>), dim3(plan.rem * C::WM), dim3(64 * C::TM * C::WN),
                      16 * C::TM * C::BN * 2, stream, part, plan.full, plan.splits, T, t_slices,
                      (long)(row1 - row0) * r, r, L2, bias, Y, ldy, row0, row1, col0, col1, act);
@@ -577,20 +588,21 @@ template <bool EXPORT>
 hipError_t dispatch(const uint8_t* qx, const float* sx, const float* T, int t_slices, int K, int r,
                     const uint16_t* L2, const uint8_t* Wq, const float* w_scales,
                     const uint16_t* bias, uint16_t* Y, int ldy, int row0, int row1, int col0,
-                    int col1, int32_t* P, float* part, int act, hipStream_t stream) {
+                    int col1, int32_t* P, const int* ewin, float* part, int act,
+                    hipStream_t stream) {
   switch (pick_tile(row1 - row0, col1 - col0)) {
     case 3:
       return launch_tile<TileBig2, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy,
-                                           row0, row1, col0, col1, P, part, act, stream);
+                                           row0, row1, col0, col1, P, ewin, part, act, stream);
     case 2:
-      return launch_tile<TileBig, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, part, act, stream);
+      return launch_tile<TileBig, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy,
+                                          row0, row1, col0, col1, P, ewin, part, act, stream);
     case 1:
-      return launch_tile<TileMed, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                          row1, col0, col1, P, part, act, stream);
+      return launch_tile<TileMed, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy,
+                                          row0, row1, col0, col1, P, ewin, part, act, stream);
     default:
-      return launch_tile<TileSmall, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, ldy, row0,
-                                            row1, col0, col1, P, part, act, stream);
+      return launch_tile<TileSmall, EXPORT>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y,
+                                            ldy, row0, row1, col0, col1, P, ewin, part, act, stream);
   }
 }
 
@@ -603,15 +615,17 @@ hipError_t launch_w4a4_gemm(const uint8_t* qx, const float* sx, const float* T, 
                             const float* w_scales, const uint16_t* bias, uint16_t* Y,
                             float* part, int act, hipStream_t stream) {
   return dispatch<false>(qx, sx, T, t_slices, K, r, L2, Wq, w_scales, bias, Y, N, 0, M, 0, N,
-                         nullptr, part, act, stream);
+                         nullptr, nullptr, part, act, stream);
 }
 
+// The forward's launch for an M x N x K problem -- its tile class, its tile
+// order and its remainder shares -- with P exported for the window instead of
+// the epilogue.  Every tile runs; only the window's entries are written.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                  int m0, int m1, int n0, int n1, int32_t* P, hipStream_t stream) {
-  (void)M;
-  (void)N;
-  return dispatch<true>(qx, nullptr, nullptr, 0, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, m0,
-                        m1, n0, n1, P, nullptr, kActNone, stream);
+  const int win[4] = {m0, m1, n0, n1};
+  return dispatch<true>(qx, nullptr, nullptr, 0, K, 0, nullptr, Wq, nullptr, nullptr, nullptr, 0, 0,
+                        M, 0, N, P, win, nullptr, kActNone, stream);
 }
 
 }  // namespace svdq

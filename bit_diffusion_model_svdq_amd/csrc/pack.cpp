@@ -236,8 +236,34 @@ void tridiag_solve(const Tridiag& t, double lambda, double tiny, std::vector<dou
   }
 }
 
+// ||T y - lambda y||_2 for the tridiagonal T.
+double tridiag_residual(const Tridiag& t, double lambda, const std::vector<double>& y) {
+  const int n = (int)t.d.size();
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double v = (t.d[i] - lambda) * y[i];
+    if (i > 0) v += t.e[i - 1] * y[i - 1];
+    if (i + 1 < n) v += t.e[i] * y[i + 1];
+    ss += v * v;
+  }
+  return sqrt(ss);
+}
+
+// Inverse iteration: kMinSweeps sweeps (each one multiplies the wanted
+// component by |lambda_i - shift| / |lambda_j - shift| against every other,
+// which after six solves leaves the vectors of small, close eigenvalues
+// accurate too), then more until the eigen-residual ||T y - lambda y|| of the
+// normalized iterate is below kResidualTol * ||T||, at most kMaxSweeps.  A
+// vector whose eigenvalue lies within `cluster` of an earlier one is
+// re-orthogonalized against that one after every solve, so a repeated
+// eigenvalue yields an orthonormal basis of its eigenspace.
+constexpr int kMinSweeps = 6;
+constexpr int kMaxSweeps = 40;
+constexpr double kResidualTol = 1e-11;
+
 // Leading r eigenvectors of the original matrix (columns of Z, n x r row-major)
-// for eigenvalues lam[0..r) (descending).  Returns false on failure.
+// for eigenvalues lam[0..r) (descending).  Returns false when an iterate stops
+// being finite or the residual test is not met within kMaxSweeps sweeps.
 bool eigenvectors(const Tridiag& t, const std::vector<double>& lam, int r,
                   std::vector<double>& Z) {
   const int n = (int)t.d.size();
@@ -245,6 +271,7 @@ bool eigenvectors(const Tridiag& t, const std::vector<double>& lam, int r,
   for (int i = 0; i < n; ++i)
     tnorm = std::max(tnorm, fabs(t.d[i]) + (i > 0 ? fabs(t.e[i - 1]) : 0.0) +
                                 (i + 1 < n ? fabs(t.e[i]) : 0.0));
+  if (!isfinite(tnorm)) return false;
   if (tnorm == 0.0) tnorm = 1.0;
   const double tiny = 2.2e-16 * tnorm;
   const double cluster = 1e-3 * tnorm;
@@ -254,7 +281,8 @@ bool eigenvectors(const Tridiag& t, const std::vector<double>& lam, int r,
     for (int i = 0; i < n; ++i)  // deterministic, non-degenerate start
       y[i] = 1.0 + 0.5 * sin(1.0 + 0.7 * i + 1.3 * j);
     const double shift = lam[j] + 4.0 * tiny * (1 + (j % 3));
-    for (int it = 0; it < 6; ++it) {
+    bool converged = false;
+    for (int it = 0; it < kMaxSweeps && !converged; ++it) {
       tridiag_solve(t, shift, tiny, y);
       // orthogonalize against earlier vectors of the same cluster
       for (int q = 0; q < j; ++q) {
@@ -268,7 +296,9 @@ bool eigenvectors(const Tridiag& t, const std::vector<double>& lam, int r,
       nrm = sqrt(nrm);
       if (!(nrm > 0.0) || !isfinite(nrm)) return false;
       for (int i = 0; i < n; ++i) y[i] /= nrm;
+      converged = it + 1 >= kMinSweeps && tridiag_residual(t, lam[j], y) <= kResidualTol * tnorm;
     }
+    if (!converged) return false;
   }
   // back-transform with the reflectors, last one first
   Z.assign((size_t)n * r, 0.0);
@@ -340,12 +370,16 @@ void gram(const std::vector<double>& Rm, int d, int o, std::vector<double>& Gm) 
 
 // ------------------------------------------------------------ quantization
 // Q of one group: scale = fl32(a/7), inv = fl32(7/a), rne codes in [-7, 7];
-// the weight scale has its two lowest significand bits cleared.
+// the weight scale has its two lowest significand bits cleared.  A group with
+// a < 2^-100 is a zero group (scale 0, codes 0): 7/a would near the float32
+// overflow, and such values are far below what the output resolves.
+constexpr float kTinyGroup = 0x1p-100f;
+
 void quantize_group(const float* v, uint8_t* packed, float* scale_out) {
   float a = 0.f;
   for (int i = 0; i < kGroup; ++i) a = std::max(a, fabsf(v[i]));
   float scale = 0.f, inv = 0.f;
-  if (a > 0.f) {
+  if (a >= kTinyGroup) {
     scale = a / 7.0f;
     inv = 7.0f / a;
   }

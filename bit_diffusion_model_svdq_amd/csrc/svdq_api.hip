@@ -2,6 +2,7 @@
 // carving, kernel dispatch.  Host-side packing lives in pack.cpp.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "svdq_internal.h"
 
@@ -24,38 +25,63 @@ svdq_status hip_check(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Workspace carve_workspace(void* base, int M, int K, int N, int r) {
-  Workspace w;
-  uint8_t* p = static_cast<uint8_t*>(base);
+WorkspaceLayout workspace_layout(int M, int K, int N, int r) {
+  WorkspaceLayout l;
   const size_t qx_bytes = align256((size_t)M * (K / 2));
   const size_t sx_bytes = align256((size_t)M * (K / kGroup) * 4);
-  w.t_slices = k1_plan(M, K, r, false).slices;
-  const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
+  l.t_slices = k1_plan(M, K, r, false).slices;
+  const size_t t_bytes = align256((size_t)l.t_slices * M * r * 4);
   const size_t part_bytes = N > 0 ? align256(gemm_split_bytes(M, K, N)) : 0;
-  w.qx = p;
-  w.sx = reinterpret_cast<float*>(p + qx_bytes);
-  w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
-  w.part = part_bytes ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes + t_bytes) : nullptr;
-  w.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
+  l.qx = 0;
+  l.sx = qx_bytes;
+  l.T = qx_bytes + sx_bytes;
+  l.part = part_bytes ? qx_bytes + sx_bytes + t_bytes : 0;
+  l.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
+  return l;
+}
+
+Workspace carve_workspace(void* base, int M, int K, int N, int r) {
+  const WorkspaceLayout l = workspace_layout(M, K, N, r);
+  uint8_t* p = static_cast<uint8_t*>(base);
+  Workspace w;
+  w.qx = p + l.qx;
+  w.sx = reinterpret_cast<float*>(p + l.sx);
+  w.T = r > 0 ? reinterpret_cast<float*>(p + l.T) : nullptr;
+  w.t_slices = l.t_slices;
+  w.part = l.part ? reinterpret_cast<float*>(p + l.part) : nullptr;
+  w.bytes = l.bytes;
   return w;
 }
 
 // MXFP4 workspace: qx [M, K/2] | sx k-tiled E8M0 bytes [ceil(K/256)][sx_rows][8]
 // | T [slices, M, r].
-MxWorkspace carve_workspace_mx(void* base, int M, int K, int N, int r) {
-  MxWorkspace w;
-  uint8_t* p = static_cast<uint8_t*>(base);
-  w.sx_rows = (M + 1) & ~1;
+WorkspaceLayout workspace_layout_mx(int M, int K, int N, int r) {
+  WorkspaceLayout l;
+  l.sx_rows = (M + 1) & ~1;
   const size_t qx_bytes = align256((size_t)M * (K / 2));
-  const size_t sx_bytes = align256((size_t)((K + 255) / 256) * w.sx_rows * 8);
-  w.t_slices = k1_plan(M, K, r, false).slices;
-  const size_t t_bytes = align256((size_t)w.t_slices * M * r * 4);
+  const size_t sx_bytes = align256((size_t)((K + 255) / 256) * l.sx_rows * 8);
+  l.t_slices = k1_plan(M, K, r, false).slices;
+  const size_t t_bytes = align256((size_t)l.t_slices * M * r * 4);
   const size_t part_bytes = N > 0 ? align256(mxfp4_gemm_split_bytes(M, K, N)) : 0;
-  w.qx = p;
-  w.sx = p + qx_bytes;
-  w.T = r > 0 ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes) : nullptr;
-  w.part = part_bytes ? reinterpret_cast<float*>(p + qx_bytes + sx_bytes + t_bytes) : nullptr;
-  w.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
+  l.qx = 0;
+  l.sx = qx_bytes;
+  l.T = qx_bytes + sx_bytes;
+  l.part = part_bytes ? qx_bytes + sx_bytes + t_bytes : 0;
+  l.bytes = qx_bytes + sx_bytes + t_bytes + part_bytes;
+  return l;
+}
+
+MxWorkspace carve_workspace_mx(void* base, int M, int K, int N, int r) {
+  const WorkspaceLayout l = workspace_layout_mx(M, K, N, r);
+  uint8_t* p = static_cast<uint8_t*>(base);
+  MxWorkspace w;
+  w.sx_rows = l.sx_rows;
+  w.qx = p + l.qx;
+  w.sx = p + l.sx;
+  w.T = r > 0 ? reinterpret_cast<float*>(p + l.T) : nullptr;
+  w.t_slices = l.t_slices;
+  w.part = l.part ? reinterpret_cast<float*>(p + l.part) : nullptr;
+  w.bytes = l.bytes;
   return w;
 }
 
@@ -66,6 +92,10 @@ using namespace svdq;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// The largest K a one-slice quantize launch stages in LDS (a multiple of 128,
+// so it holds for MXFP4 too); include/svdq.h states the same bound.
+constexpr int kMaxCanonicalK = 12544;
 
 svdq_status check_shapes(int M, int K, int N, int r, bool need_n) {
   if (M < 1) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 1 (got %d)", M);
@@ -211,10 +241,43 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
 
 extern "C" {
 
+
 size_t svdq_forward_workspace_bytes(int M, int K, int N, int r) {
   if (M < 1 || K < kGroup || K % kGroup || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16)
     return 0;
-  return carve_workspace(nullptr, M, K, N, r).bytes;
+  return workspace_layout(M, K, N, r).bytes;
+}
+
+svdq_status svdq_forward_workspace_layout(int M, int K, int N, int r, size_t* qx_offset,
+                                          size_t* sx_offset, size_t* t_offset, int* t_slices) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, N, r, true));
+    if (!qx_offset || !sx_offset || !t_offset || !t_slices)
+      return fail(SVDQ_ERR_INVALID_ARG, "NULL output pointer");
+    const WorkspaceLayout l = workspace_layout(M, K, N, r);
+    *qx_offset = l.qx;
+    *sx_offset = l.sx;
+    *t_offset = r > 0 ? l.T : 0;
+    *t_slices = r > 0 ? l.t_slices : 0;
+    return SVDQ_OK;
+  });
+}
+
+svdq_status svdq_forward_workspace_layout_mxfp4(int M, int K, int N, int r, size_t* qx_offset,
+                                                size_t* sx_offset, size_t* t_offset, int* t_slices,
+                                                int* sx_rows) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, N, r));
+    if (!qx_offset || !sx_offset || !t_offset || !t_slices || !sx_rows)
+      return fail(SVDQ_ERR_INVALID_ARG, "NULL output pointer");
+    const WorkspaceLayout l = workspace_layout_mx(M, K, N, r);
+    *qx_offset = l.qx;
+    *sx_offset = l.sx;
+    *t_offset = r > 0 ? l.T : 0;
+    *t_slices = r > 0 ? l.t_slices : 0;
+    *sx_rows = l.sx_rows;
+    return SVDQ_OK;
+  });
 }
 
 svdq_status svdq_forward_quantize(const uint16_t* X, int M, int K, int r, const float* smooth,
@@ -283,9 +346,26 @@ svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const flo
     SVDQ_TRY(check_ptr(qx, "qx", false));
     SVDQ_TRY(check_ptr(sx, "sx", false));
     SVDQ_TRY(check_ptr(T, "T", r == 0));
+    if (!k1_one_slice_fits(K, r))
+      return fail(SVDQ_ERR_INVALID_ARG,
+                  "K=%d: the canonical-layout quantize stages a whole row in LDS and takes K <= %d",
+                  K, kMaxCanonicalK);
     return hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, qx, sx, T, true,
                                                    static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down launch");
+  });
+}
+
+svdq_status svdq_act_absmax_update_device(const uint16_t* X, int64_t M, int K, float* amax,
+                                          void* stream) {
+  return guarded([&]() -> svdq_status {
+    if (M < 0 || K < 1)
+      return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld K=%d", (long long)M, K);
+    if (!amax || (M > 0 && !X)) return fail(SVDQ_ERR_INVALID_ARG, "NULL buffer");
+    if ((reinterpret_cast<uintptr_t>(X) & 1) || (reinterpret_cast<uintptr_t>(amax) & 3))
+      return fail(SVDQ_ERR_ALIGNMENT, "X must be 2-byte and amax 4-byte aligned");
+    return hip_check(launch_act_absmax(X, M, K, amax, static_cast<hipStream_t>(stream)),
+                     "act_absmax launch");
   });
 }
 
@@ -307,7 +387,7 @@ svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int 
 
 size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r) {
   if (M < 1 || K < 128 || K % 128 || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16) return 0;
-  return carve_workspace_mx(nullptr, M, K, N, r).bytes;
+  return workspace_layout_mx(M, K, N, r).bytes;
 }
 
 svdq_status svdq_forward_quantize_mxfp4(const uint16_t* X, int M, int K, int r,
@@ -380,13 +460,21 @@ svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, con
     SVDQ_TRY(check_ptr(qx, "qx", false));
     SVDQ_TRY(check_ptr(sx_e8m0, "sx_e8m0", false));
     SVDQ_TRY(check_ptr(T, "T", r == 0));
+    if (!k1_one_slice_fits(K, r))
+      return fail(SVDQ_ERR_INVALID_ARG,
+                  "K=%d: the canonical-layout quantize stages a whole row in LDS and takes K <= %d",
+                  K, kMaxCanonicalK);
     return hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, qx, sx_e8m0, T, true,
                                                       0, static_cast<hipStream_t>(stream)),
                      "smooth_quant_lora_down (MXFP4) launch");
   });
 }
 
-const char* svdq_status_string(svdq_status s) {
+const char* svdq_status_string(svdq_status status) {
+  // callers may pass any int (the ABI carries the enum as one): read its bytes
+  // as an int, since loading an out-of-range value as the enum type is undefined
+  int s;
+  memcpy(&s, &status, sizeof(s));
   switch (s) {
     case SVDQ_OK: return "ok";
     case SVDQ_ERR_INVALID_ARG: return "invalid argument";

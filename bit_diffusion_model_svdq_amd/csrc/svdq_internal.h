@@ -15,6 +15,16 @@ constexpr int kMaxRank = 128;   // rank bound of the low-rank branch
 
 svdq_status hip_check(hipError_t e, const char* what);
 
+// Byte offsets of the workspace's parts (and its size), computed without a base
+// pointer; the MXFP4 layout also fixes the row count of its k-tiled scales.
+struct WorkspaceLayout {
+  size_t qx = 0, sx = 0, T = 0, part = 0, bytes = 0;
+  int t_slices = 1;
+  int sx_rows = 0;
+};
+WorkspaceLayout workspace_layout(int M, int K, int N, int r);
+WorkspaceLayout workspace_layout_mx(int M, int K, int N, int r);
+
 // Workspace carving: qx [M, K/2] | sx [M, K/64] | T [slices, M, r] | split partials
 // (only when k2 splits a last partial wave of tiles; N = 0 leaves them out),
 // each part 256-byte aligned.
@@ -57,6 +67,9 @@ struct K1Plan {
   int rtm = 1, slices = 1, gslice = 1;
 };
 K1Plan k1_plan(int M, int K, int r, bool one_slice);
+// Whether a one-slice launch (a whole row of K channels per workgroup, as the
+// canonical-layout entry points use) fits the kernel's LDS budget.
+bool k1_one_slice_fits(int K, int r);
 hipError_t launch_smooth_quant_lora_down(const uint16_t* X, int M, int K, int r,
                                          const float* smooth, const uint16_t* L1, uint8_t* qx,
                                          float* sx, float* T, bool one_slice, hipStream_t stream);
@@ -97,6 +110,10 @@ hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_r
                              int t_slices, int M, int K, int N, int r, const uint16_t* L2,
                              const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
                              uint16_t* Y, float* part, int act, hipStream_t stream);
+
+// Calibration statistic: amax[k] = max(amax[k], max_m |X[m,k]|) on the GPU
+// (unsigned atomic max of float32 bit patterns; amax must hold values >= +0).
+hipError_t launch_act_absmax(const uint16_t* X, int64_t M, int K, float* amax, hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

@@ -30,8 +30,9 @@
  * Codes are in [-7, 7]; -8 is never produced.
  *
  * Quantization of one group v[0..63] (float32):
- *   a = max|v|; a == 0 -> scale 0, codes 0; else scale = fl32(a / 7),
- *   inv = fl32(7 / a), code = clamp(round_half_even(fl32(v * inv)), -7, 7).
+ *   a = max|v|; a < 2^-100 (zero included) -> scale 0, codes 0; else
+ *   scale = fl32(a / 7), inv = fl32(7 / a),
+ *   code = clamp(round_half_even(fl32(v * inv)), -7, 7).
  *   A weight scale then has its two lowest significand bits cleared.
  * Smoothed activations: x_hat[m,k] = fl32(X[m,k] * fl32(1 / s[k])).
  *
@@ -127,6 +128,17 @@ svdq_status svdq_append_lora(const float* smooth, int K, int N, const uint16_t* 
  * aligned.  Returns 0 for shapes the forward rejects. */
 size_t svdq_forward_workspace_bytes(int M, int K, int N, int r);
 
+/* Where the forward keeps stage 1's results inside its workspace, as byte
+ * offsets from the workspace's start: qx [M, K/2] codes at *qx_offset, the
+ * float32 scales sx [M, K/64] at *sx_offset, and *t_slices partial sums of
+ * T = x_hat L1^T, each [M, r] float32, back to back from *t_offset (T is their
+ * sum taken in slice order; *t_slices = 0 and *t_offset = 0 when r = 0).  The
+ * layout depends on the shape only.  Host function; SVDQ_ERR_INVALID_ARG for
+ * shapes the forward rejects or NULL outputs.  For callers that inspect or
+ * reuse the quantized activations (and for tests of the forward's own launch). */
+svdq_status svdq_forward_workspace_layout(int M, int K, int N, int r, size_t* qx_offset,
+                                          size_t* sx_offset, size_t* t_offset, int* t_slices);
+
 /* The SVDQuant linear forward (E4): launches the fused smooth + quantize +
  * lora_down kernel, then the W4A4 GEMM whose epilogue applies the group
  * scales, adds the lora_up product and the bias and stores bf16 Y.
@@ -174,16 +186,36 @@ svdq_status svdq_forward_gemm_act(int M, int K, int N, int r, const uint16_t* L2
 
 /* Stage 1 into caller buffers in the canonical layouts: Q(X diag(s)^-1) as
  * qx [M, K/2] and sx [M, K/64], and T = x_hat L1^T [M, r] in float32
- * (T may be NULL when r == 0).  Device memory, asynchronous. */
+ * (T may be NULL when r == 0).  One workgroup stages a whole row of K channels
+ * in LDS, so K <= 12544 here (larger K: SVDQ_ERR_INVALID_ARG; the forward
+ * itself slices K and has no such bound).  Device memory, asynchronous. */
 svdq_status svdq_quantize_activations(const uint16_t* X, int M, int K, const float* smooth,
                                       const uint16_t* L1, int r, uint8_t* qx, float* sx,
                                       float* T, void* stream);
 
+/* The calibration statistic of svdq_act_absmax_update on the GPU: A_scale of
+ * E2 (Terminology Entry, section 2.3: the per-channel absolute maximum of the
+ * activations).  Folds M rows of bf16 activations X [M, K] (device memory,
+ * row-major) into the running maximum amax [K] (device memory, float32):
+ * amax[k] = max(amax[k], max_m |X[m,k]|), bit-identical to the host function
+ * (a max does not depend on the order of evaluation).  amax must hold values
+ * >= +0 on entry (start from zeros): the partial maxima meet through an
+ * unsigned atomic max of the float32 bit patterns, which orders those values
+ * like floats.  Any K >= 1; M = 0 does nothing.  X must be 2-byte aligned and
+ * amax 4-byte aligned (SVDQ_ERR_ALIGNMENT).  Asynchronous on `stream`; calls
+ * that write the same amax may run concurrently (the atomics commute). */
+svdq_status svdq_act_absmax_update_device(const uint16_t* X, int64_t M, int K, float* amax,
+                                          void* stream);
+
 /* The integer group partial sums of Q(x_hat) Q(R) (E4, E7) over the output
- * block rows [m0, m1) x columns [n0, n1), computed by the same MFMA main loop
- * the forward runs: P[(m-m0), (n-n0), g] = sum_{k in group g} qx[m,k] qw[n,k],
- * int32 [(m1-m0), (n1-n0), K/64].  Requires 0 <= m0 < m1 <= M,
- * 0 <= n0 < n1 <= N, N % 16 == 0, K % 64 == 0.  Device memory, asynchronous. */
+ * block rows [m0, m1) x columns [n0, n1), computed by the forward's own GEMM
+ * launch for an M x N x K layer (the same tile class, tile order and, where
+ * the forward cuts a last partial wave of tiles along K, the same shares):
+ * every tile runs its MFMA main loop, and the tiles that cover the block write
+ * P[(m-m0), (n-n0), g] = sum_{k in group g} qx[m,k] qw[n,k] instead of the
+ * scale epilogue, int32 [(m1-m0), (n1-n0), K/64].  qx [M, K/2] and Wq [N, K/2]
+ * are read whole.  Requires 0 <= m0 < m1 <= M, 0 <= n0 < n1 <= N,
+ * N % 16 == 0, K % 64 == 0.  Device memory, asynchronous. */
 svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                       int m0, int m1, int n0, int n1, int32_t* P, void* stream);
 
@@ -224,6 +256,12 @@ svdq_status svdq_quantize_residual_mxfp4(const float* W, int N, int K, const flo
 /* Workspace of the MXFP4 forward: codes, E8M0 scales and T; 0 for rejected shapes. */
 size_t svdq_forward_workspace_bytes_mxfp4(int M, int K, int N, int r);
 
+/* The MXFP4 workspace, as svdq_forward_workspace_layout: the E8M0 activation
+ * scales at *sx_offset are k-tiled, [ceil(K/256)][*sx_rows][8] bytes. */
+svdq_status svdq_forward_workspace_layout_mxfp4(int M, int K, int N, int r, size_t* qx_offset,
+                                                size_t* sx_offset, size_t* t_offset, int* t_slices,
+                                                int* sx_rows);
+
 /* The MXFP4 forward: quantize + lora_down, then the block-scaled GEMM whose
  * epilogue adds the lora_up product and the bias.  w_e8m0 is k-tiled
  * [ceil(K/256)][N][8] (see above); the workspace holds the activation scales
@@ -256,7 +294,8 @@ svdq_status svdq_forward_gemm_act_mxfp4(int M, int K, int N, int r, const uint16
                                         const void* workspace, size_t workspace_bytes,
                                         void* stream);
 
-/* Stage 1 into canonical buffers: qx [M, K/2], sx_e8m0 [M, K/32], T [M, r]. */
+/* Stage 1 into canonical buffers: qx [M, K/2], sx_e8m0 [M, K/32], T [M, r];
+ * K <= 12544 as for svdq_quantize_activations. */
 svdq_status svdq_quantize_activations_mxfp4(const uint16_t* X, int M, int K, const float* smooth,
                                             const uint16_t* L1, int r, uint8_t* qx,
                                             uint8_t* sx_e8m0, float* T, void* stream);

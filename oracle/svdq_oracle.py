@@ -36,7 +36,10 @@ design notes):
   R is formed from the rounded factors;
   Q is symmetric 4-bit, one float32 scale per 64 consecutive input channels,
   scale = fl32(amax / 7), codes = clamp(rne(fl32(v * fl32(7 / amax))), -7, 7),
-  an all-zero group gets scale 0 and codes 0;
+  an all-zero group gets scale 0 and codes 0, and so does a group whose amax
+  lies below 2^-100 (there fl32(7 / amax) would approach the float32 overflow
+  at about 2^-125.5; such a group's values are below anything the layer's
+  output resolves);
   a weight scale additionally has its two lowest significand bits cleared
   (rounded toward zero), so that 3 * scale is exact in float32;
   x_hat = fl32(X * fl32(1 / s));
@@ -53,6 +56,7 @@ import numpy as np
 
 GROUP = 64
 QMAX = 7
+TINY_GROUP = 2.0 ** -100    # absmax below this: coded as a zero group
 S_MIN = 1e-5
 STAT_FLOOR = 1e-5
 
@@ -201,7 +205,8 @@ def quantize_groups(v32, weight_scale: bool = False):
 
     [Term] 2.3 (E4) names Q; [Abs] fixes 4 bits.  Symmetric, codes in
     [-7, 7]:  a = max|v|;  scale = fl32(a / 7);  inv = fl32(7 / a);
-    q = clamp(rne(fl32(v * inv)), -7, 7).  a == 0 gives scale 0, q 0.
+    q = clamp(rne(fl32(v * inv)), -7, 7).  a < 2^-100 (a == 0 included)
+    gives scale 0, q 0.
     weight_scale=True clears the two lowest significand bits of the scale.
     Returns (codes int8 [..., K], scales float32 [..., K/64]).
     """
@@ -210,7 +215,7 @@ def quantize_groups(v32, weight_scale: bool = False):
     assert K % GROUP == 0
     g = v.reshape(v.shape[:-1] + (K // GROUP, GROUP))
     a = np.max(np.abs(g), axis=-1)
-    nz = a > 0
+    nz = a >= F32(TINY_GROUP)
     safe = np.where(nz, a, F32(1))
     scale = np.where(nz, safe / F32(QMAX), F32(0)).astype(F32)
     inv = np.where(nz, F32(QMAX) / safe, F32(0)).astype(F32)

@@ -107,6 +107,67 @@ def test_pack_exact_lowrank_weight_leaves_zero_residual():
     assert float(np.max(pl["w_scales"])) < 1e-30
 
 
+def _exact_spectrum_weight(N, K, sigma):
+    """W = U diag(sigma) V^T with U, V columns of Sylvester-Hadamard matrices scaled to
+    unit length (N, K powers of 4, so 1/sqrt is a power of two) and dyadic sigma: every
+    entry is a short dyadic sum, exact in float32, so the float32 W has exactly these
+    singular values, repeated ones included."""
+    from scipy.linalg import hadamard
+    p = len(sigma)
+    U = hadamard(N)[:, 1:p + 1] / np.sqrt(N)
+    V = hadamard(K)[:, 1:p + 1] / np.sqrt(K)
+    W64 = (U * np.asarray(sigma)[None, :]) @ V.T
+    W = W64.astype(F32)
+    assert np.array_equal(W.astype(F64), W64)
+    return W, U, V
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (256, 64)])
+def test_pack_degenerate_singular_values_at_the_rank_boundary(N, K):
+    """sigma_r = sigma_(r+1) (and a repeated pair inside the kept rank): the rank-r
+    subspace is not unique, so only invariants are checked ([Term] 2.3, E5 and E6):
+    the library's singular values are the designed ones, their squares sum to
+    ||W_hat||_F^2, the lora_down rows are orthonormal and span v_1..v_15 plus a unit
+    vector of the degenerate plane (nothing outside v_1..v_17), and the residual energy
+    ||W_hat - L2 L1||_F^2 is the tail sum up to the bf16 rounding of the factors.
+    Exercises both Gram sides (N < K and K < N) and the re-orthogonalization of
+    inverse iteration inside a cluster."""
+    r = 16
+    sigma = np.array([8, 7, 6, 6, 5.5, 5, 4.5, 4, 3.75, 3.5, 3.25, 3, 2.75, 2.5, 2.25, 2, 2,
+                      1.75, 1.5, 1.25, 1, 0.75, 0.5, 0.25])
+    assert sigma[r - 1] == sigma[r] and sigma[2] == sigma[3]
+    W, U, V = _exact_spectrum_weight(N, K, sigma)
+    A = O.weight_absmax(W)                         # A == W_scale -> s = 1 for alpha = 1/2
+    pl = S.svdq_pack_weights(W, A, 0.5, r, want_sigma=True)
+    np.testing.assert_array_equal(pl["smooth"], np.ones(K, F32))
+    sg = pl["sigma"]
+    np.testing.assert_allclose(sg[:len(sigma)], sigma, rtol=1e-12, atol=1e-12 * sigma[0])
+    assert np.all(sg[len(sigma):] < 1e-6 * sigma[0])
+    Wd = W.astype(F64)
+    assert abs(np.sum(sg ** 2) - np.sum(Wd ** 2)) <= 1e-12 * np.sum(Wd ** 2)
+    L1 = O.bf16_to_f64(pl["L1"])                   # [r, K]
+    L2 = O.bf16_to_f64(pl["L2"])                   # [N, r]
+    bf = 2.0 ** -8                                 # bf16 relative rounding, with margin
+    assert np.max(np.abs(L1 @ L1.T - np.eye(r))) <= 4 * bf
+    # nothing outside span(v_1 .. v_17)
+    V17 = V[:, :r + 1]
+    out = L1.T - V17 @ (V17.T @ L1.T)
+    assert np.linalg.norm(out) <= 4 * bf * np.sqrt(r)
+    # v_1 .. v_15 lie in the row space of L1
+    V15 = V[:, :r - 1]
+    Q, _ = np.linalg.qr(L1.T)
+    miss = V15 - Q @ (Q.T @ V15)
+    assert np.linalg.norm(miss) <= 4 * bf * np.sqrt(r)
+    # residual energy: the tail sum of squares, up to the rounding of the factors
+    tail = float(np.sum(sigma[r:] ** 2))
+    res = float(np.sum((Wd - L2 @ L1) ** 2))
+    assert abs(res - tail) <= 0.02 * tail
+    # the residual the library quantized is that of its own rounded factors
+    Wq, ws = S.svdq_quantize_residual(W, pl["smooth"], pl["L1"], pl["L2"])
+    np.testing.assert_array_equal(Wq, pl["Wq"])
+    np.testing.assert_array_equal(ws, pl["w_scales"])
+
+
 @pytest.mark.slow
 def test_pack_weights_dit_projection_shape():
     w = synth.WORKLOADS["dit_proj"]
@@ -180,6 +241,30 @@ def test_workspace_bytes():
     assert S.svdq_forward_workspace_bytes(M, K, N, 24) == 0
 
 
+def test_workspace_layout_matches_the_workspace_size():
+    """Offsets of qx, sx and the T slices: the parts in that order, 256-byte aligned,
+    the T slices of the quantize kernel's plan (2 at the DiT projection, 5 at the MLP
+    down projection, 1 where a second slice would cost the GEMM more)."""
+    al = lambda x: (x + 255) // 256 * 256
+    for (M, K, N, r, slices) in [(4096, 3072, 3072, 32, 2), (4608, 12288, 3072, 32, 5),
+                                 (256, 1024, 1024, 16, 1), (4608, 3072, 9216, 48, 1), (77, 192, 48, 0, 0)]:
+        lay = S.svdq_forward_workspace_layout(M, K, N, r)
+        assert lay["qx"] == 0
+        assert lay["sx"] == al(M * K // 2)
+        assert lay["t_slices"] == slices
+        if r:
+            assert lay["T"] == al(M * K // 2) + al(M * K // 64 * 4)
+            assert lay["T"] + slices * M * r * 4 <= S.svdq_forward_workspace_bytes(M, K, N, r)
+        mx = S.svdq_forward_workspace_layout(M, K, N, r, mxfp4=True) if K % 128 == 0 else None
+        if mx:
+            assert mx["sx"] == al(M * K // 2) and mx["sx_rows"] == M + (M & 1)
+            assert mx["t_slices"] == slices
+    with pytest.raises(S.SvdqError):
+        S.svdq_forward_workspace_layout(4096, 100, 3072, 32)
+    with pytest.raises(S.SvdqError):
+        S.svdq_forward_workspace_layout(64, 192, 64, 16, mxfp4=True)
+
+
 def test_device_entry_points_validate_before_launching():
     """Each case fails validation, so nothing reaches the GPU runtime."""
     L = S._lib
@@ -205,6 +290,18 @@ def test_device_entry_points_validate_before_launching():
     assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 0, 300, 0, 16, a, None) == 1
     assert L.svdq_debug_group_partials(a, a, 256, 1024, 1024, 10, 10, 0, 16, a, None) == 1
     assert L.svdq_debug_group_partials(a, mis, 256, 1024, 1024, 0, 16, 0, 16, a, None) == 3
+    # the canonical-layout quantize stages a whole row in LDS: K <= 12544, any rank
+    for r_ in (0, 16, 128):
+        assert L.svdq_quantize_activations(a, 16, 12608, a, a, r_, a, a, a, None) == 1
+        assert "12544" in S.svdq_last_error()
+        assert L.svdq_quantize_activations_mxfp4(a, 16, 12672, a, a, r_, a, a, a, None) == 1
+    assert L.svdq_act_absmax_update_device(a, -1, 64, a, None) == 1
+    assert L.svdq_act_absmax_update_device(a, 8, 0, a, None) == 1
+    assert L.svdq_act_absmax_update_device(None, 8, 64, a, None) == 1
+    assert L.svdq_act_absmax_update_device(a, 8, 64, None, None) == 1
+    assert L.svdq_act_absmax_update_device(a + 1, 8, 64, a, None) == 3
+    assert L.svdq_act_absmax_update_device(a, 8, 64, a + 2, None) == 3
+    assert L.svdq_act_absmax_update_device(a, 0, 64, a, None) == 0   # empty batch: nothing to launch
 
 
 def test_append_lora_bit_exact_with_oracle():

@@ -109,8 +109,11 @@ def test_unknown_activation_rejected():
     with pytest.raises(S.SvdqError) as e:
         gpu_linear(dev(p["X"]), d, p["M"], p["K"], p["N"], p["r"], 7, False)
     assert e.value.status == 1
-    with pytest.raises(S.SvdqError):
-        gpu_linear(dev(p["X"]), d, p["M"], p["K"], p["N"], p["r"], -1, True)
+    pm = dict(p)
+    pm["Wq"], pm["w_scales"] = O.quantize_residual_mx(p["W"], p["s"], p["L1"], p["L2"])
+    with pytest.raises(S.SvdqError) as e:
+        gpu_linear(dev(p["X"]), layer_to_device(pm), p["M"], p["K"], p["N"], p["r"], -1, True)
+    assert e.value.status == 1
 
 
 @pytest.mark.parametrize("mx", [False, True], ids=["int4", "mxfp4"])

@@ -116,6 +116,30 @@ def test_k1_codes_scales_bit_exact_and_T(name):
     assert O.rel_fro(T, T_o) <= T_REL_FRO
 
 
+def test_k1_tiny_groups_bit_exact():
+    """Groups far below the normal range (s = 1, so x_hat = X): an absmax below 2^-100 (all
+    bf16 subnormals, or 2^-101) is a zero group, an absmax of exactly 2^-100 is coded as the
+    same group scaled up would be; normal groups around them are unaffected."""
+    say("k1 tiny groups")
+    g = np.random.default_rng(91)
+    M, K = 32, 512
+    X = np.clip(g.standard_normal((M, K)), -3.9, 3.9).astype(F32)
+    X[:, 0:64] = (X[:, 0:64] * 1e-39).astype(F32)                 # bf16 subnormals
+    X[:, 64:128] = (X[:, 64:128] / 4 * 2.0 ** -100).astype(F32)
+    X[:, 64] = F32(2.0 ** -100)                                    # absmax exactly 2^-100
+    X[:, 128:192] = (X[:, 128:192] / 4 * 2.0 ** -101).astype(F32)  # absmax below 2^-101
+    X[:, 192:256] = (X[:, 192:256] * 2.0 ** -99).astype(F32)
+    Xb = synth.f32_to_bf16_bits(X)
+    s = np.ones(K, F32)
+    p = dict(X=Xb, s=s, L1=np.zeros((0, K), np.uint16), r=0, M=M, K=K)
+    d = dict(X=dev(Xb), s=dev(s), L1=None)
+    qx, sx, _ = run_k1(p, d)
+    qx_o, sx_o, _, _ = O.quantize_activations(Xb, s)
+    np.testing.assert_array_equal(qx, qx_o)
+    np.testing.assert_array_equal(sx.view(np.uint32), sx_o.view(np.uint32))
+    assert np.all(sx_o[:, 0] == 0) and np.all(sx_o[:, 2] == 0) and np.all(sx_o[:, 1] > 0)
+
+
 def test_k1_power_of_two_equivariance_on_gpu():
     p = dict(packed("tiny"))
     d = to_device(p)

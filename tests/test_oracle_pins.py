@@ -214,6 +214,35 @@ def test_quantizer_error_bound_and_range():
     assert np.all((F32(3) * sc).astype(F64) == 3.0 * sc.astype(F64))
 
 
+def test_quantizer_tiny_groups():
+    """The reading for groups far below float32's normal range: absmax < 2^-100 is a zero
+    group (7/a would near the float32 overflow at about 2^-125.5, and 0 * inf would be NaN).
+    At and above 2^-100 the codes are those of the same group scaled up by a power of two
+    (equivariance holds exactly there, subnormal members included) and the scale is the
+    scaled group's scale scaled back."""
+    g = np.random.default_rng(77)
+    base = np.clip(g.standard_normal((3, 64)) * 3, -4.9, 4.9).astype(F32)
+    base[:, 0] = 5.0                                # a fixed absmax: scaled groups hit the threshold exactly
+    base[1, 1:8] = 1e-30                            # members that go subnormal when scaled down
+    q0, s0 = O.quantize_groups(base)
+    at = (base.astype(F64) * 2.0 ** -100 / 5.0).astype(F32)     # absmax exactly 2^-100
+    assert np.all(np.max(np.abs(at), axis=1) == F32(2.0 ** -100))
+    q1, s1 = O.quantize_groups(at)
+    scaled = (at.astype(F64) * 2.0 ** 100).astype(F32)
+    q1s, s1s = O.quantize_groups(scaled)
+    np.testing.assert_array_equal(q1, q1s)
+    assert np.all(s1 == (s1s.astype(F64) * 2.0 ** -100).astype(F32))
+    below = (at.astype(F64) / 2).astype(F32)        # absmax 2^-101, members deep in subnormals
+    q2, s2 = O.quantize_groups(below)
+    assert np.all(q2 == 0) and np.all(s2 == 0)
+    sub = np.full((1, 64), F32(1e-40))              # an all-subnormal group
+    sub[0, ::2] *= -1
+    q3, s3 = O.quantize_groups(sub)
+    assert np.all(q3 == 0) and np.all(s3 == 0)
+    with np.errstate(all="raise"):                  # no overflow, no 0 * inf anywhere
+        O.quantize_groups(np.concatenate([at, below, sub]))
+
+
 def test_quantizer_power_of_two_equivariance():
     g = synth.rng_for("tiny", 5)
     v = g.standard_normal((8, 256)).astype(F32)
@@ -379,7 +408,7 @@ def _q_exact(vals, weight):
     """Q of one 64-group with exact rationals: scale fl32(a/7) (weights: two low
     significand bits cleared), inv fl32(7/a), q = clamp(rne(fl32(v inv)), -7, 7)."""
     a = max(abs(v) for v in vals)
-    if a == 0:
+    if a < Fraction(2) ** -100:          # a zero group, as the contract reads it
         return [0] * len(vals), Fraction(0)
     scale = _rn32(a / 7)
     if weight:
@@ -638,6 +667,76 @@ def test_mx_forward_matches_exact_rationals():
                 sl = slice(32 * blk, 32 * blk + 32)
                 acc += sum(a * w for a, w in zip(q_block(xv[m, sl]), q_block(W[n, sl])))
             assert Fr(Y[m, n]) == acc
+
+
+@pytest.mark.parametrize("K,r", [(64, 1), (128, 2)])
+def test_mx_forward_with_lowrank_branch_matches_exact_rationals(K, r):
+    """The MXFP4 forward with its low-rank branch and bias, brute force with Fractions
+    ([Term] 2.3, E4: both terms): smoothing by power-of-two s, the residual
+    R = W diag(s) - L2 L1 rounded once to float32, block exponents from each block's
+    absmax, nearest E2M1 values, T = x_hat L1^T and T L2^T.  The exact T and the exact
+    Y must equal the oracle's (dyadic inputs keep every float64 sum exact), so a
+    transposed L2, T taken from X instead of x_hat, a dropped term or a residual of
+    the wrong sign fails here."""
+    from fractions import Fraction as Fr
+    g = np.random.default_rng(300 + K + r)
+    M, N = 2, 3
+    X = synth.f32_to_bf16_bits((g.integers(-64, 64, (M, K)) / 16.0).astype(F32))
+    s = np.ldexp(np.ones(K, F32), g.integers(-2, 3, K)).astype(F32)
+    W = (g.integers(-64, 64, (N, K)) / 32.0).astype(F32)
+    L1 = synth.f32_to_bf16_bits((g.integers(-8, 8, (r, K)) / 8.0).astype(F32))
+    L2 = synth.f32_to_bf16_bits((g.integers(-8, 8, (N, r)) / 4.0).astype(F32))
+    b = synth.f32_to_bf16_bits((g.integers(-8, 8, N) / 8.0).astype(F32))
+    # the branch must matter: x_hat differs from X, and L2 is not symmetric in use
+    assert np.any(s != 1)
+
+    mags = [Fr(0), Fr(1, 2), Fr(1), Fr(3, 2), Fr(2), Fr(3), Fr(4), Fr(6)]
+
+    def q_block(vals):
+        amax = max(abs(v) for v in vals)
+        e = -127
+        if amax:
+            fl = 0
+            while Fr(2) ** (fl + 1) <= amax:
+                fl += 1
+            while Fr(2) ** fl > amax:
+                fl -= 1
+            e = fl - 2
+        out = []
+        for v in vals:
+            y = abs(v) / Fr(2) ** e
+            d = [abs(y - m) for m in mags]
+            best = min(range(8), key=lambda i: (d[i], i % 2))
+            out.append((-1 if v < 0 else 1) * mags[best] * Fr(2) ** e)
+        return out, e
+
+    xv = [[Fr(float(v)) for v in row] for row in O.bf16_to_f64(X)]
+    sv = [Fr(float(v)) for v in s]
+    l1 = [[Fr(float(v)) for v in row] for row in O.bf16_to_f64(L1)]
+    l2 = [[Fr(float(v)) for v in row] for row in O.bf16_to_f64(L2)]
+    bv = [Fr(float(v)) for v in O.bf16_to_f64(b)]
+    xh = [[x * Fr(float(_rn32(1 / sk))) for x, sk in zip(row, sv)] for row in xv]
+    R = [[Fr(float(_rn32(Fr(float(W[n, k])) * sv[k] - sum(l2[n][j] * l1[j][k] for j in range(r)))))
+          for k in range(K)] for n in range(N)]
+    T = [[sum(xh[m][k] * l1[j][k] for k in range(K)) for j in range(r)] for m in range(M)]
+
+    qx, sxe, T_o, _ = O.quantize_activations_mx(X, s, L1)
+    Wq, we = O.quantize_residual_mx(W, s, L1, L2)
+    Y = O.forward_mx(X, s, L1, L2, Wq, we, b)
+    assert T_o.shape == (M, r)
+    for m in range(M):
+        for j in range(r):
+            assert Fr(T_o[m, j]) == T[m][j]
+    for m in range(M):
+        for n in range(N):
+            acc = bv[n] + sum(T[m][j] * l2[n][j] for j in range(r))
+            for blk in range(K // 32):
+                sl = slice(32 * blk, 32 * blk + 32)
+                qa, ea = q_block(xh[m][sl])
+                qw, ew = q_block(R[n][sl])
+                assert sxe[m, blk] == ea + 127 and we[n, blk] == ew + 127
+                acc += sum(a * w for a, w in zip(qa, qw))
+            assert abs(Fr(Y[m, n]) - acc) <= abs(acc) * Fr(1, 10 ** 15)
 
 
 # ------------------------------------------------------------- GELU (tanh form)
