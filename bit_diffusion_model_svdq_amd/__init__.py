@@ -50,7 +50,7 @@ EXPORTS = [
     "svdq_linear_forward_act", "svdq_forward_gemm_act", "svdq_linear_forward_act_mxfp4",
     "svdq_forward_gemm_act_mxfp4", "svdq_mxfp4_tiled_scale_bytes", "svdq_mxfp4_tile_scales",
     "svdq_act_absmax_update_device", "svdq_forward_workspace_layout",
-    "svdq_forward_workspace_layout_mxfp4",
+    "svdq_forward_workspace_layout_mxfp4", "svdq_static_workspace_bytes", "svdq_linear_forward_noalloc",
 ]
 
 # svdq_activation
@@ -85,6 +85,8 @@ _sig = {
     "svdq_debug_group_partials": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P],
     "svdq_act_absmax_update_device": [_P, ctypes.c_int64, _I, _P, _P],
     "svdq_forward_workspace_layout": [_I, _I, _I, _I, _P, _P, _P, _P],
+    "svdq_static_workspace_bytes": [],
+    "svdq_linear_forward_noalloc": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_layout_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P],
     "svdq_quantize_residual_mxfp4": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_bytes_mxfp4": [_I, _I, _I, _I],
@@ -106,6 +108,7 @@ for _name, _args in _sig.items():
     _f.argtypes = _args
     _f.restype = _I
 _lib.svdq_forward_workspace_bytes.restype = ctypes.c_size_t
+_lib.svdq_static_workspace_bytes.restype = ctypes.c_size_t
 _lib.svdq_forward_workspace_bytes_mxfp4.restype = ctypes.c_size_t
 _lib.svdq_mxfp4_tiled_scale_bytes.restype = ctypes.c_size_t
 _lib.svdq_status_string.restype = ctypes.c_char_p
@@ -318,6 +321,23 @@ def svdq_linear_forward_act(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y
                                       _dp(w_scales), _dp(bias), int(activation), _dp(Y), _dp(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "svdq_linear_forward_act")
+    return Y
+
+
+def svdq_static_workspace_bytes() -> int:
+    return int(_lib.svdq_static_workspace_bytes())
+
+
+def svdq_linear_forward_noalloc(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y, stream=None):
+    """svdq_linear_forward_act without a workspace argument: the library's static device
+    workspace serves instead (no allocation; calls that overlap on one GPU race)."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y)
+    st = _lib.svdq_linear_forward_noalloc(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                          _dp(w_scales), _dp(bias), int(activation), _dp(Y), _stream(stream))
+    _check(st, "svdq_linear_forward_noalloc")
     return Y
 
 

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -237,10 +239,59 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
                    "mxfp4_gemm launch");
 }
 
+// ---- the allocation-free forward's workspace
+// A file-scope device array serves as the forward's workspace for callers
+// that cannot allocate.  Host code never uses the array's name as an address
+// (on the host it only names the symbol); the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+svdq_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  SVDQ_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SVDQ_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    SVDQ_TRY(hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!ptr) return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVDQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
+size_t svdq_static_workspace_bytes(void) { return kScratchBytes; }
+
+svdq_status svdq_linear_forward_noalloc(const uint16_t* X, int M, int K, int N, int r,
+                                        const float* smooth, const uint16_t* L1,
+                                        const uint16_t* L2, const uint8_t* Wq,
+                                        const float* w_scales, const uint16_t* bias,
+                                        int activation, uint16_t* Y, void* stream) {
+  return guarded([&]() -> svdq_status {
+    // the same checks as the workspace entry point, then the size bound
+    SVDQ_TRY(check_shapes(M, K, N, r, true));
+    const size_t need = workspace_layout(M, K, N, r).bytes;
+    if (need > kScratchBytes)
+      return fail(SVDQ_ERR_WORKSPACE,
+                  "M=%d K=%d N=%d r=%d needs %zu workspace bytes; the static workspace holds %zu",
+                  M, K, N, r, need, kScratchBytes);
+    void* ws = nullptr;
+    SVDQ_TRY(scratch_for_current_device(&ws));
+    return linear_forward(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, activation, Y, ws,
+                          kScratchBytes, stream);
+  });
+}
 
 size_t svdq_forward_workspace_bytes(int M, int K, int N, int r) {
   if (M < 1 || K < kGroup || K % kGroup || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16)

@@ -169,6 +169,25 @@ svdq_status svdq_linear_forward_act(const uint16_t* X, int M, int K, int N, int 
                                     const uint16_t* bias, int activation, uint16_t* Y,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as svdq_linear_forward_act, with its workspace (the activation codes,
+ * scales, T and the GEMM's split partials) in a static device array of
+ * svdq_static_workspace_bytes() bytes (64 MiB) that each GPU the library runs
+ * on holds until the process ends.  Shapes whose workspace,
+ * svdq_forward_workspace_bytes(M, K, N, r), exceeds it return
+ * SVDQ_ERR_WORKSPACE before anything is launched.  No allocation and no
+ * synchronization; nothing in the array needs to start at zero.  Every call on
+ * one GPU shares that GPU's array and it keeps the last call's contents, so
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race: serialize them.  Otherwise as svdq_linear_forward_act. */
+size_t svdq_static_workspace_bytes(void);
+svdq_status svdq_linear_forward_noalloc(const uint16_t* X, int M, int K, int N, int r,
+                                        const float* smooth, const uint16_t* L1,
+                                        const uint16_t* L2, const uint8_t* Wq,
+                                        const float* w_scales, const uint16_t* bias,
+                                        int activation, uint16_t* Y, void* stream);
+
 /* The two halves of svdq_linear_forward, for callers that schedule or time
  * them separately.  Stage 1 writes qx, sx, T into the workspace; stage 2
  * reads them and writes Y.  Same requirements as svdq_linear_forward. */

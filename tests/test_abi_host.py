@@ -295,6 +295,16 @@ def test_device_entry_points_validate_before_launching():
         assert L.svdq_quantize_activations(a, 16, 12608, a, a, r_, a, a, a, None) == 1
         assert "12544" in S.svdq_last_error()
         assert L.svdq_quantize_activations_mxfp4(a, 16, 12672, a, a, r_, a, a, a, None) == 1
+    # the allocation-free forward: shapes checked, then its workspace need against the
+    # static array, all before any HIP call (nothing here has a GPU)
+    na = lambda M=256, K=1024, N=1024, r=16: L.svdq_linear_forward_noalloc(
+        a, M, K, N, r, a, a, a, a, a, a, 0, a, None)
+    assert S.svdq_static_workspace_bytes() == 64 << 20
+    assert na(K=1000) == 1
+    assert na(r=24) == 1
+    assert S.svdq_forward_workspace_bytes(4608, 12288, 3072, 32) > 64 << 20
+    assert na(M=4608, K=12288, N=3072, r=32) == 4
+    assert "static workspace" in S.svdq_last_error()
     assert L.svdq_act_absmax_update_device(a, -1, 64, a, None) == 1
     assert L.svdq_act_absmax_update_device(a, 8, 0, a, None) == 1
     assert L.svdq_act_absmax_update_device(None, 8, 64, a, None) == 1
