@@ -11,11 +11,14 @@ Prints one JSON line (rank 0).  Default workload: the DiT attention
 projection, M=4096 tokens, K=N=3072, rank 32.  Other workloads (--workload)
 are the small-K UNet widths and the DiT MLP linears.
 
-Timing.  W eager warm-up steps, then K eager steps with HIP events around
-every launch (per-kernel durations as the stream sees them, dispatch gaps
-included).  Then, unless --no-graph, the same K steps are captured into one
-HIP graph and replayed once, untimed, and once timed: `value` and
-`ms_per_step` come from that replay (the launch path a serving loop would
+Timing.  First the clocks settle: untimed steps for --settle-ms of wall time
+(the host-side pack leaves the GPU idle, and a few warm-up steps are not
+enough for the engine clock to ramp).  Then W eager warm-up steps, then K
+eager steps with HIP events around every launch (per-kernel durations as the
+stream sees them, dispatch gaps included).  Then, unless --no-graph, the same
+K steps are captured into one HIP graph, replayed untimed for 150 ms (the
+capture idles the GPU and the clock drops), and replayed once timed: `value`
+and `ms_per_step` come from that replay (the launch path a serving loop would
 use).  Per-kernel durations for the roofline come from graphs of K
 back-to-back launches of that kernel alone over the same rotating buffers.
 --workload dit_block times the four SVDQuant linears of a DiT block at width
@@ -59,6 +62,14 @@ def parse():
     ap.add_argument("--format", choices=["int4", "mxfp4"], default="int4",
                     help="int4: symmetric int4, one fp32 scale per 64 channels (int8 MFMA); "
                          "mxfp4: E2M1 with an E8M0 scale per 32 (block-scaled FP4 MFMA)")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed steps for this much wall time before the warm-up, so that the "
+                         "engine clock has ramped when timing starts")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="token rows M (default: the workload's own)")
+    ap.add_argument("--path", choices=["auto", "two-kernel"], default="auto",
+                    help="auto: the forward's own plan (one fused kernel for narrow layers); "
+                         "two-kernel: the quantize kernel then the GEMM, always")
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager launch loop instead of the HIP graph replay")
     return ap.parse_args()
@@ -98,6 +109,59 @@ def load_traffic(kernel_file: str, workload: str):
     return None
 
 
+def read_sclk_mhz():
+    """The engine clock's current DPM level (MHz) from sysfs, or None where it is not readable."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def settle(torch, launch, ms):
+    """Untimed launch(i) in chunks of 10 until `ms` of wall time has passed; returns
+    (launches, wall ms)."""
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            launch(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def host_cpu():
+    """nproc (the CPUs this process may run on) and the CPU model, for the baseline's record."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"nproc": nproc, "cpu_model": model}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
+
+
 def copy_probe():
     import torch
     n = 256 << 20
@@ -128,12 +192,12 @@ def main():
     if args.workload == "dit_block":
         return bench_block(args, S, synth, torch)
     w = synth.WORKLOADS[args.workload]
-    M, K, N, r = w.M, w.K, w.N, w.rank
+    M, K, N, r = (args.tokens or w.M), w.K, w.N, w.rank
     dev = torch.device("cuda:0")
 
     # ---- offline pack (host, untimed) through the library's packer
     t0 = time.time()
-    X = synth.activations(w)
+    X = synth.activations(w, M)
     W = synth.weight(w)
     b = synth.bias(w)
     A = np.zeros(K, np.float32)
@@ -167,10 +231,17 @@ def main():
     quantize = S.svdq_forward_quantize_mxfp4 if mx else S.svdq_forward_quantize
     gemm = S.svdq_forward_gemm_mxfp4 if mx else S.svdq_forward_gemm
 
-    def step(d):
-        quantize(d["X"], d["s"], d["L1"], d["work"])
-        gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+    # narrow int4 layers run as one fused kernel: the step is then the forward call itself
+    fused = (not mx) and args.path == "auto" and S.svdq_forward_fused(M, K, N, r)
 
+    def step(d):
+        if fused:
+            S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"])
+        else:
+            quantize(d["X"], d["s"], d["L1"], d["work"])
+            gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+
+    settle_n, settle_ms = settle(torch, lambda i: step(sets[i % nsets]), args.settle_ms)
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
@@ -187,11 +258,17 @@ def main():
         d = sets[i % nsets]
         e = ev[i]
         e[0].record()
-        quantize(d["X"], d["s"], d["L1"], d["work"])
-        e[1].record()
-        gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
-        e[2].record()
+        if fused:
+            step(d)
+            e[1].record()
+            e[2].record()
+        else:
+            quantize(d["X"], d["s"], d["L1"], d["work"])
+            e[1].record()
+            gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
+            e[2].record()
     end.record()
+    sclk_eager = read_sclk_mhz()   # sampled while the queued steps run
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
@@ -210,13 +287,20 @@ def main():
             d = sets[i % nsets]
             gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
 
-        ms_step = time_graph(torch, lambda i: step(sets[i % nsets]), args.steps)
-        k1_ms = time_graph(torch, k1_only, args.steps)
-        k2_ms = time_graph(torch, k2_only, args.steps)
+        graph_clock = []
+        ms_step = time_graph(torch, lambda i: step(sets[i % nsets]), args.steps, graph_clock)
+        if fused:
+            k1_ms = ms_step
+        else:
+            k1_ms = time_graph(torch, k1_only, args.steps)
+            k2_ms = time_graph(torch, k2_only, args.steps)
         graph_info = {"steps_per_graph": args.steps, "ms_per_step": round(ms_step, 5),
                       "eager_ms_per_step": round(eager_ms_step, 5),
-                      "eager_k1_us": round(eager_k1_ms * 1e3, 3), "eager_k2_us": round(eager_k2_ms * 1e3, 3)}
+                      "eager_k1_us": round(eager_k1_ms * 1e3, 3), "eager_k2_us": round(eager_k2_ms * 1e3, 3),
+                      "sclk_mhz": graph_clock[0]}
 
+    if fused:   # the two-kernel figures below are placeholders, replaced by the fused kernel's
+        k2_ms = k1_ms
     ops_main = 2.0 * M * N * K                 # the 4-bit product (int8 or FP4 MFMA)
     ops_low = 2.0 * M * r * (K + N)            # bf16 low-rank branch
     tops = (ops_main + ops_low) / (ms_step * 1e-3) / 1e12
@@ -258,6 +342,7 @@ def main():
                   if mx else "int4 codes on int8 MFMA (int32 acc), fp32 epilogue, bf16 low-rank + output"),
         "data": "synthetic",
         "config": {"workload": args.workload, "format": args.format, "M": M, "K": K, "N": N, "rank": r,
+                   "path": "fused" if fused else "two-kernel",
                    "group": 32 if mx else 64, "rotated_sets": nsets, "hip_graph": not args.no_graph},
         "tokens_per_s": round(tokens_s, 1),
         "pct_mfma_peak": round(100.0 * tops / peak_mfma, 2),
@@ -284,18 +369,48 @@ def main():
                         "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)},
         },
         "graph": graph_info,
+        "clock": {"settle_steps": settle_n, "settle_ms": round(settle_ms, 1), "sclk_mhz_eager": sclk_eager,
+                  "source": "pp_dpm_sclk (current DPM level)"},
         "wall_s_timed": round(wall, 4),
         "pack_s": round(pack_s, 2),
     }
+
+    if fused:   # one kernel: it is the dominant one, and k1/k2 do not run
+        fb = (M * K * 2 + N * K // 2 + N * (K // 64) * 4 + r * K * 2 + N * r * 2 + K * 4 + 2 * N
+              + M * N * 2)
+        f_bound = "mfma" if ops_main / (peak_mfma * 1e12) >= fb / (PEAK_HBM_GBS * 1e9) else "hbm"
+        f_gbs = fb / (k1_ms * 1e-3) / 1e9
+        f_tops = ops_main / (k1_ms * 1e-3) / 1e12
+        f_ach, f_peak, f_unit = (f_tops, peak_mfma, "TFLOP/s") if f_bound == "mfma" else \
+            (f_gbs, PEAK_HBM_GBS, "GB/s")
+        out["roofline"] = {
+            "kernel": "w4a4_fused_smallk (quantize + lora_down + GEMM + lora_up in one kernel)",
+            "bound": f_bound, "achieved": round(f_ach, 2), "peak": f_peak, "unit": f_unit,
+            "frac": round(f_ach / f_peak, 4), "algorithmic": {"ops": ops_main, "bytes": fb},
+            "traffic": load_traffic("k12_fused_smallk.hip", args.workload),
+            "avg_launch_us": round(k1_ms * 1e3, 3)}
+        out["kernels"] = {"w4a4_fused_smallk": {
+            "avg_launch_us": round(k1_ms * 1e3, 3), "algorithmic_bytes": fb, "achieved_GBs": round(f_gbs, 1),
+            "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(f_gbs / PEAK_HBM_GBS, 4), "ops": ops_main,
+            "achieved_TOPS": round(f_tops, 2), "pct_mfma_peak": round(100.0 * f_tops / peak_mfma, 2)}}
+        if graph_info:
+            graph_info.pop("eager_k2_us", None)
+            graph_info["eager_fused_us"] = graph_info.pop("eager_k1_us")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, X, pk, b, args.cpu_seconds, mx)
     print(json.dumps(out), flush=True)
 
 
-def time_graph(torch, launch, n):
-    """Capture launch(0..n-1) into one HIP graph, replay it once untimed, then once
-    between HIP events on the current stream; returns ms per launch(i)."""
+GRAPH_SETTLE_MS = 150.0
+
+
+def time_graph(torch, launch, n, clock=None):
+    """Capture launch(0..n-1) into one HIP graph, replay it untimed for
+    GRAPH_SETTLE_MS of wall time (at least once: the capture leaves the GPU idle
+    and the engine clock drops meanwhile), then once between HIP events on the
+    current stream; returns ms per launch(i).  If `clock` is a list, the engine
+    clock read while the timed replay runs is appended."""
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -307,12 +422,18 @@ def time_graph(torch, launch, n):
     with torch.cuda.graph(g):
         for i in range(n):
             launch(i)
+    t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < GRAPH_SETTLE_MS:
+        g.replay()
+        torch.cuda.synchronize()
     gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gs.record()
     g.replay()
     ge.record()
+    if clock is not None:
+        clock.append(read_sclk_mhz())
     torch.cuda.synchronize()
     ms = gs.elapsed_time(ge) / n
     del g
@@ -389,6 +510,7 @@ def bench_block(args, S, synth, torch):
         if ev is not None:
             ev[2 * len(layers)].record()
 
+    settle_n, settle_ms = settle(torch, lambda i: run(sets[i % nsets]), args.settle_ms)
     for i in range(args.warmup):
         run(sets[i % nsets])
     torch.cuda.synchronize()
@@ -401,6 +523,7 @@ def bench_block(args, S, synth, torch):
     for i in range(args.steps):
         run(sets[i % nsets], evs[i])
     end.record()
+    sclk_eager = read_sclk_mhz()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = eager_ms_step = start.elapsed_time(end) / args.steps
@@ -467,6 +590,8 @@ def bench_block(args, S, synth, torch):
                      "avg_launch_us": dom_us},
         "kernels": kern,
         "wall_s_timed": round(wall, 4),
+        "clock": {"settle_steps": settle_n, "settle_ms": round(settle_ms, 1), "sclk_mhz_eager": sclk_eager,
+                  "source": "pp_dpm_sclk (current DPM level)"},
         "pack_s": round(pack_s, 2),
     }
     if not args.no_cpu_baseline:
@@ -477,11 +602,7 @@ def bench_block(args, S, synth, torch):
 def cpu_baseline_block(layers, seconds, mx):
     """The CPU oracle on the same few token rows through the four layers (its own chain)."""
     from oracle import svdq_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = 1
+    cores = blas_threads()
     fwd = O.forward_mx if mx else O.forward
     rows, dt = 4, 0.0
     for _ in range(5):
@@ -499,7 +620,7 @@ def cpu_baseline_block(layers, seconds, mx):
         rows = int(min(256, max(rows + 1, rows * min(8.0, 1.2 * seconds / max(dt, 1e-3)))))
     ops = sum(2.0 * rows * L["N"] * L["K"] + 2.0 * rows * L["r"] * (L["K"] + L["N"]) for L in layers)
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(rows / dt, 2),
-            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "cores": cores, **host_cpu(), "kind": "oracle", "seconds": round(dt, 2),
             "sample": (f"{rows} token rows through the four block linears (full K and N, r=48), float64 numpy "
                        f"oracle chain on host cores")}
 
@@ -507,11 +628,7 @@ def cpu_baseline_block(layers, seconds, mx):
 def cpu_baseline(w, X, pk, b, seconds, mx=False):
     """The CPU oracle (as it stands) on a bounded sample of rows of the same workload."""
     from oracle import svdq_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = 1
+    cores = blas_threads()
     fwd = O.forward_mx if mx else O.forward
     # grow the sample until it takes about `seconds` (whole workload, repeated, if it is smaller)
     rows, passes, dt = 16, 1, 0.0
@@ -523,15 +640,15 @@ def cpu_baseline(w, X, pk, b, seconds, mx=False):
         if dt >= 0.5 * seconds or passes >= 8:
             break
         grow = min(8.0, 1.2 * seconds / max(dt, 1e-3))
-        if rows < w.M:
-            rows = int(min(w.M, max(rows + 1, rows * grow)))
+        if rows < X.shape[0]:
+            rows = int(min(X.shape[0], max(rows + 1, rows * grow)))
         else:
             passes = int(min(8, max(passes + 1, passes * grow)))
     done = rows * passes
     ops = 2.0 * done * w.N * w.K + 2.0 * done * w.rank * (w.K + w.N)
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "tokens_per_s": round(done / dt, 2),
-            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": (f"{rows} of {w.M} token rows of {w.name} x {passes} pass(es) (full K={w.K}, N={w.N}, "
+            "cores": cores, **host_cpu(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": (f"{rows} of {X.shape[0]} token rows of {w.name} x {passes} pass(es) (full K={w.K}, N={w.N}, "
                        f"r={w.rank}), float64 numpy oracle forward on host cores")}
 
 

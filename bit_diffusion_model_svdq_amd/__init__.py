@@ -51,6 +51,7 @@ EXPORTS = [
     "svdq_forward_gemm_act_mxfp4", "svdq_mxfp4_tiled_scale_bytes", "svdq_mxfp4_tile_scales",
     "svdq_act_absmax_update_device", "svdq_forward_workspace_layout",
     "svdq_forward_workspace_layout_mxfp4", "svdq_static_workspace_bytes", "svdq_linear_forward_noalloc",
+    "svdq_forward_fused", "svdq_debug_fused_forward",
 ]
 
 # svdq_activation
@@ -86,6 +87,8 @@ _sig = {
     "svdq_act_absmax_update_device": [_P, ctypes.c_int64, _I, _P, _P],
     "svdq_forward_workspace_layout": [_I, _I, _I, _I, _P, _P, _P, _P],
     "svdq_static_workspace_bytes": [],
+    "svdq_forward_fused": [_I, _I, _I, _I],
+    "svdq_debug_fused_forward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P],
     "svdq_linear_forward_noalloc": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_layout_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P],
     "svdq_quantize_residual_mxfp4": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
@@ -396,6 +399,27 @@ def svdq_act_absmax_update_device(X, amax, stream=None):
     st = _lib.svdq_act_absmax_update_device(_dp(X), M, K, _dp(amax), _stream(stream))
     _check(st, "svdq_act_absmax_update_device")
     return amax
+
+
+def svdq_forward_fused(M, K, N, r) -> bool:
+    """Whether the int4 forward runs (M, K, N, r) as the single fused small-K kernel."""
+    return bool(_lib.svdq_forward_fused(int(M), int(K), int(N), int(r)))
+
+
+def svdq_debug_fused_forward(X, smooth, L1, L2, Wq, w_scales, bias, activation, Y, qx, sx, stream=None):
+    """The fused small-K forward, also writing its activation codes qx [M, K/2] and scales sx [M, K/64]."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y)
+    _need(qx, "qx", ("uint8",), (M, K // 2))
+    _need(sx, "sx", ("float32",), (M, K // 64))
+    _same_device(X, qx, sx)
+    st = _lib.svdq_debug_fused_forward(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                       _dp(w_scales), _dp(bias), int(activation), _dp(Y), _dp(qx), _dp(sx),
+                                       _stream(stream))
+    _check(st, "svdq_debug_fused_forward")
+    return Y
 
 
 def svdq_debug_group_partials(qx, Wq, m0, m1, n0, n1, P, stream=None):

@@ -31,7 +31,7 @@ CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fopenmp",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 HIP_SOURCES = ["svdq_api.hip", "k1_smooth_quant.hip", "k2_w4a4_gemm.hip", "k2_mxfp4_gemm.hip",
-               "calib_absmax.hip"]
+               "calib_absmax.hip", "k12_fused_smallk.hip"]
 CXX_SOURCES = ["pack.cpp"]
 
 

@@ -32,11 +32,9 @@
 // vector-memory counter with a load still to be waited for, and HBM sees full
 // lines instead of 16-byte pieces from different waves.
 //
-// Quantization.  The group absmax is a local max plus two cross-lane steps.
-// Rounding to the integer code uses the float32 adder: for |y| <= 7.0000005,
-// fl32(y + 1.5 * 2^23) = 1.5 * 2^23 + rne(y) exactly, so the low nibble of its
-// bit pattern is the packed code.  |y| cannot exceed 7 * (1 + 2^-24) because
-// inv = fl32(7 / amax), so no clamp is needed.
+// Quantization (int4).  The arithmetic is quant_core.h's, shared with the
+// fused small-K forward: the group absmax over the four lanes of a row, the
+// float32 scale amax / 7 and the rounding adder that yields the codes.
 //
 // MXFP4 (template flag MX).  The same kernel quantizes each block of 32
 // channels (a lane's 8 + the 3 other lanes of its row) to FP4 E2M1 with one
@@ -57,6 +55,7 @@
 // order (deterministic).
 #include <algorithm>
 
+#include "quant_core.h"
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -69,7 +68,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kW = 8;                  // waves per workgroup
 constexpr int kThreads = kW * 64;
-constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
 constexpr size_t kLdsBudget = 152 * 1024;
 constexpr int kMaxSliceGroups = 48;    // the plan below never cuts longer slices
 constexpr int kMaxRT2 = 5;             // two row tiles per block up to r = 80 (register budget)
@@ -82,18 +80,6 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
   __builtin_memcpy(&r, &v, 16);
   return r;
-}
-
-// Two codes per byte from the rounding adder's results (low nibble = even channel).
-__device__ inline uint32_t nib2(float ze, float zo) {
-  const uint32_t e = __float_as_uint(ze), o = __float_as_uint(zo);
-  return (e & 0x0Fu) | ((o << 4) & 0xF0u);
-}
-
-__device__ inline uint32_t pack8(const float* z) {  // 8 codes -> one dword
-  const uint32_t b0 = nib2(z[0], z[1]), b1 = nib2(z[2], z[3]);
-  const uint32_t b2 = nib2(z[4], z[5]), b3 = nib2(z[6], z[7]);
-  return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
 }
 
 // groups in flight per wave
@@ -253,17 +239,11 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       float amax = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      // a group below 2^-100 (zero included) is a zero group: scale 0, codes 0
-      const bool coded = amax >= 0x1p-100f;
-      scale = coded ? __float_as_uint(amax / 7.0f) : 0u;
-      const float inv = coded ? 7.0f / amax : 0.f;
+      amax = quant::row_group_absmax(amax);
       float z[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) z[i] = xh[i] * inv + kRound;  // two roundings: product, then code
-      codes.x = pack8(z);
-      codes.y = pack8(z + 8);
+      quant::int4_codes<16>(xh, amax, scale, z);
+      codes.x = quant::pack8(z);
+      codes.y = quant::pack8(z + 8);
     }
     if constexpr (RT > 0) {
       uint32_t hi[8], lo[8];

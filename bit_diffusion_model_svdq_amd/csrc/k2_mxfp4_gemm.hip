@@ -300,19 +300,6 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
       act);
 }
 
-int cu_count_mx() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <class C>
 int tiles_of(int rows, int cols) {
   return ((rows + C::BM - 1) / C::BM) * ((cols + C::BN - 1) / C::BN);
@@ -350,7 +337,7 @@ template <class C>
 MxSplit plan_split(int M, int N, int K) {
   MxSplit p;
   const int tiles = tiles_of<C>(M, N);
-  const int cus = cu_count_mx() * C::WPE;
+  const int cus = device_cu_count() * C::WPE;
   const int ksteps = K / KS;
   p.full = tiles;
   const int rem = tiles % cus;
@@ -397,7 +384,7 @@ hipError_t launch(const uint8_t* qx, const uint8_t* sx, int sx_rows, const float
 // (measured 9-10 % faster on the 4608-token QKV and up projections, 12 %
 // slower than the split on the down projection).
 int pick_tile(int M, int N, int K) {
-  const int cus = cu_count_mx();
+  const int cus = device_cu_count();
   const int big = tiles_of<MxBig>(M, N);
   if (big >= cus) {
     const int rem = big % cus;

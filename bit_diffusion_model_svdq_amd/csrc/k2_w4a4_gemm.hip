@@ -472,19 +472,6 @@ __global__ __launch_bounds__(64 * C::TM * C::WN) void w4a4_fixup_kernel(
       col0, col1, act, lds);
 }
 
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <class C, bool EXPORT, int MODE>
 hipError_t set_lds_attr() {
   static bool done = false;  // benign race: every caller sets the same value
@@ -510,7 +497,7 @@ int tiles_of(int rows, int cols) {
 // other's compute (measured 3-9 % faster on the 4608-token DiT layers, and
 // 2 % slower where 256 x 192 tiles fill whole waves, which keep them).
 int pick_tile(int rows, int cols) {
-  const int cus = cu_count();
+  const int cus = device_cu_count();
   const int big = tiles_of<TileBig>(rows, cols);
   if (big >= cus) return big % cus ? 3 : 2;
   if (tiles_of<TileMed>(rows, cols) >= cus) return 1;
@@ -531,7 +518,7 @@ template <class C>
 SplitPlan plan_split(int M, int N, int K) {
   SplitPlan p;
   const int tiles = tiles_of<C>(M, N);
-  const int cus = cu_count() * C::WPE;
+  const int cus = device_cu_count() * C::WPE;
   const int stages = (K / kGroup + GS - 1) / GS;
   p.full = tiles;
   const int rem = tiles % cus;

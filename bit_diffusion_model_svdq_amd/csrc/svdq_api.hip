@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "svdq_internal.h"
@@ -23,6 +24,19 @@ svdq_status fail(svdq_status st, const char* fmt, ...) {
 svdq_status hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return SVDQ_OK;
   return fail(SVDQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];   // zero-initialized: 0 = not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -196,6 +210,11 @@ svdq_status linear_forward(const uint16_t* X, int M, int K, int N, int r, const 
   if (workspace_bytes < w.bytes)
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const FusedPlan fp = fused_plan(M, K, N, r);
+  if (fp.use)
+    return hip_check(launch_fused_smallk(fp, X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y,
+                                         act, nullptr, nullptr, s),
+                     "fused small-K forward launch");
   SVDQ_TRY(hip_check(launch_smooth_quant_lora_down(X, M, K, r, smooth, L1, w.qx, w.sx, w.T, false, s),
                      "smooth_quant_lora_down launch"));
   return hip_check(launch_w4a4_gemm(w.qx, w.sx, w.T, w.t_slices, M, K, N, r, L2, Wq, w_scales,
@@ -433,6 +452,34 @@ svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int 
     return hip_check(
         launch_group_partials(qx, Wq, M, N, K, m0, m1, n0, n1, P, static_cast<hipStream_t>(stream)),
         "group_partials launch");
+  });
+}
+
+int svdq_forward_fused(int M, int K, int N, int r) {
+  if (M < 1 || K < kGroup || K % kGroup || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16)
+    return 0;
+  return fused_plan(M, K, N, r).use ? 1 : 0;
+}
+
+svdq_status svdq_debug_fused_forward(const uint16_t* X, int M, int K, int N, int r,
+                                     const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                     const uint8_t* Wq, const float* w_scales,
+                                     const uint16_t* bias, int activation, uint16_t* Y,
+                                     uint8_t* qx, float* sx, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes(M, K, N, r, true));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, w_scales, bias, Y));
+    SVDQ_TRY(check_act(activation));
+    SVDQ_TRY(check_ptr(qx, "qx", false));
+    SVDQ_TRY(check_ptr(sx, "sx", false));
+    const FusedPlan fp = fused_plan(M, K, N, r);
+    if (!fp.use)
+      return fail(SVDQ_ERR_INVALID_ARG, "M=%d K=%d N=%d r=%d does not take the fused small-K path", M, K,
+                  N, r);
+    return hip_check(launch_fused_smallk(fp, X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y,
+                                         activation, qx, sx, static_cast<hipStream_t>(stream)),
+                     "fused small-K forward launch");
   });
 }
 

@@ -15,6 +15,9 @@ constexpr int kMaxRank = 128;   // rank bound of the low-rank branch
 
 svdq_status hip_check(hipError_t e, const char* what);
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
+
 // Byte offsets of the workspace's parts (and its size), computed without a base
 // pointer; the MXFP4 layout also fixes the row count of its k-tiled scales.
 struct WorkspaceLayout {
@@ -114,6 +117,23 @@ hipError_t launch_mxfp4_gemm(const uint8_t* qx, const uint8_t* sx_e8m0, int sx_r
 // Calibration statistic: amax[k] = max(amax[k], max_m |X[m,k]|) on the GPU
 // (unsigned atomic max of float32 bit patterns; amax must hold values >= +0).
 hipError_t launch_act_absmax(const uint16_t* X, int64_t M, int K, float* amax, hipStream_t stream);
+
+// The fused small-K forward: quantize, lora_down, the W4A4 GEMM, lora_up, bias
+// and activation in one kernel (K <= 1280, r <= 32, N <= 2560, and at most 256
+// blocks of 16 x 16 outputs x 64 channels per compute unit).  nt: column
+// tiles of 16 per wave (a workgroup covers 128 nt columns of 16 rows).
+struct FusedPlan {
+  bool use = false;
+  int nt = 0;
+};
+FusedPlan fused_plan(int M, int K, int N, int r);
+// dbg_qx / dbg_sx (both NULL, or both set): the codes ([M, K/2] packed) and
+// scales ([M, K/64]) the kernel quantized, written by the first column slice.
+hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, int K, int N, int r,
+                               const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                               const uint8_t* Wq, const float* w_scales, const uint16_t* bias,
+                               uint16_t* Y, int act, uint8_t* dbg_qx, float* dbg_sx,
+                               hipStream_t stream);
 
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,

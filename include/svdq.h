@@ -141,7 +141,11 @@ svdq_status svdq_forward_workspace_layout(int M, int K, int N, int r, size_t* qx
 
 /* The SVDQuant linear forward (E4): launches the fused smooth + quantize +
  * lora_down kernel, then the W4A4 GEMM whose epilogue applies the group
- * scales, adds the lora_up product and the bias and stores bf16 Y.
+ * scales, adds the lora_up product and the bias and stores bf16 Y.  Small
+ * layers (svdq_forward_fused(M, K, N, r) != 0: K <= 1280, r <= 32,
+ * N <= 2560 and at most 256 blocks of 16 x 16 outputs x 64 channels per
+ * compute unit) run all of it as one kernel instead; the codes and scales
+ * are the same, the workspace is then unused (but still required).
  * Requires M >= 1, K % 64 == 0, N % 16 == 0, 0 <= r <= 128, r % 16 == 0,
  * 16-byte aligned device pointers (bias and, for r = 0, L1/L2 may be NULL)
  * and workspace_bytes >= svdq_forward_workspace_bytes(M, K, N, r).  Asynchronous
@@ -237,6 +241,23 @@ svdq_status svdq_act_absmax_update_device(const uint16_t* X, int64_t M, int K, f
  * N % 16 == 0, K % 64 == 0.  Device memory, asynchronous. */
 svdq_status svdq_debug_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                       int m0, int m1, int n0, int n1, int32_t* P, void* stream);
+
+/* 1 if the int4 forward (svdq_linear_forward[_act], and the no-alloc entry
+ * point) runs the shape as the single fused small-K kernel, else 0 (also for
+ * shapes the forward rejects).  Host only. */
+int svdq_forward_fused(int M, int K, int N, int r);
+
+/* The fused small-K forward exactly as svdq_linear_forward_act launches it,
+ * also writing the activation codes it quantized, qx [M, K/2] (packed as
+ * svdq_quantize_activations writes them), and their scales sx [M, K/64], so
+ * that they can be checked against the quantizer's definition (E2, E3).
+ * SVDQ_ERR_INVALID_ARG if svdq_forward_fused(M, K, N, r) is 0.  Device memory,
+ * asynchronous; the forward's own requirements otherwise (no workspace). */
+svdq_status svdq_debug_fused_forward(const uint16_t* X, int M, int K, int N, int r,
+                                     const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                     const uint8_t* Wq, const float* w_scales,
+                                     const uint16_t* bias, int activation, uint16_t* Y,
+                                     uint8_t* qx, float* sx, void* stream);
 
 /* ------------------------------------------------------- MXFP4 variant
  * The same layer with Q(.) (Terminology Entry, section 2.3, E4) taken as the

@@ -63,3 +63,17 @@ def test_stored_traffic_is_dropped_when_the_source_changes(tmp_path, monkeypatch
     assert bench.load_traffic(kernel, workload) == entry["bytes_per_launch"]
     monkeypatch.setattr(bench, "kernel_source_hash", lambda name: "0" * 16)
     assert bench.load_traffic(kernel, workload) is None
+
+
+def test_host_cpu_record():
+    """cpu_baseline's host fields: the CPUs this process may use and the CPU model."""
+    h = bench.host_cpu()
+    assert isinstance(h["nproc"], int) and h["nproc"] >= 1
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
+    assert bench.blas_threads() >= 1
+
+
+def test_sclk_reader_tolerates_missing_sysfs():
+    """The engine-clock reading is an int (MHz) or None, never an exception."""
+    v = bench.read_sclk_mhz()
+    assert v is None or (isinstance(v, int) and v > 0)

@@ -366,8 +366,15 @@ def test_forward_without_bias_and_deterministic():
     check_y(Y1, Yref, "tiny no bias")
 
 
-def test_forward_stages_match_fused_call():
-    p = packed("smallk_640")
+@pytest.mark.parametrize("name,M", [("dit_proj", 1024), ("smallk_640", None), ("smallk_640", 1024)])
+def test_forward_stages_match_the_forward_call(name, M):
+    """svdq_forward_quantize then svdq_forward_gemm against svdq_linear_forward.
+    Where the forward runs those two stages (the DiT projection, 1024 tokens), the
+    outputs are identical bit for bit.  Where it runs the fused small-K kernel
+    (1024 x 640 -> 640), the fused kernel sums T = x_hat L1^T in another order, so
+    both results are held to the oracle instead (the codes of the two paths are
+    compared bit for bit by the fused kernel's own tests)."""
+    p = packed(name, M=M)
     d = to_device(p)
     Yf = run_forward(p, d)
     M, K, N, r = p["M"], p["K"], p["N"], p["r"]
@@ -376,7 +383,13 @@ def test_forward_stages_match_fused_call():
     S.svdq_forward_quantize(d["X"], d["s"], d["L1"], ws)
     S.svdq_forward_gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], Y, ws, r)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(O.bf16_to_f64(host(Y, np.uint16)), Yf)
+    Ys = O.bf16_to_f64(host(Y, np.uint16))
+    if not S.svdq_forward_fused(M, K, N, r):
+        np.testing.assert_array_equal(Ys, Yf)
+    else:
+        Yref = O.forward(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"])
+        check_y(Ys, Yref, f"{name} two stages")
+        check_y(Yf, Yref, f"{name} fused forward")
 
 
 def test_forward_in_hip_graph_replays_match_eager():
