@@ -324,6 +324,8 @@ def main():
         metric = "fused W4A4+low-rank linear TOPS and tokens/s at M=4096,K=N=3072,r=32 (% MFMA peak)"
     else:
         metric = f"fused {kind}+low-rank linear TOPS and tokens/s at M={M},K={K},N={N},r={r} (% MFMA peak)"
+    # stored traffic is keyed by workload, format and (when overridden) token rows
+    tkey = args.workload + (f"_m{M}" if M != w.M else "") + ("_mxfp4" if mx else "")
     k1_file, k2_file = ("k1_smooth_quant.hip", "k2_mxfp4_gemm.hip") if mx else \
         ("k1_smooth_quant.hip", "k2_w4a4_gemm.hip")
 
@@ -354,14 +356,14 @@ def main():
             "unit": k2_unit,
             "frac": round(k2_achieved / k2_peak, 4),
             "algorithmic": {"ops": ops_main, "bytes": k2_bytes},
-            "traffic": load_traffic(k2_file, args.workload + ("_mxfp4" if mx else "")),
+            "traffic": load_traffic(k2_file, tkey),
             "avg_launch_us": round(k2_ms * 1e3, 3),
         },
         "kernels": {
             "k1_smooth_quant_lora_down": {"avg_launch_us": round(k1_ms * 1e3, 3), "bound": "hbm",
                                           "algorithmic_bytes": k1_bytes, "achieved_GBs": round(k1_gbs, 1),
                                           "peak_GBs": PEAK_HBM_GBS, "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
-                                          "traffic": load_traffic(k1_file, args.workload + ("_mxfp4" if mx else ""))},
+                                          "traffic": load_traffic(k1_file, tkey)},
             "k2_gemm": {"avg_launch_us": round(k2_ms * 1e3, 3), "ops": ops_main,
                         "achieved_TOPS": round(k2_tops, 2),
                         "pct_mfma_peak": round(100.0 * k2_tops / peak_mfma, 2),
@@ -387,7 +389,7 @@ def main():
             "kernel": "w4a4_fused_smallk (quantize + lora_down + GEMM + lora_up in one kernel)",
             "bound": f_bound, "achieved": round(f_ach, 2), "peak": f_peak, "unit": f_unit,
             "frac": round(f_ach / f_peak, 4), "algorithmic": {"ops": ops_main, "bytes": fb},
-            "traffic": load_traffic("k12_fused_smallk.hip", args.workload),
+            "traffic": load_traffic("k12_fused_smallk.hip", tkey),
             "avg_launch_us": round(k1_ms * 1e3, 3)}
         out["kernels"] = {"w4a4_fused_smallk": {
             "avg_launch_us": round(k1_ms * 1e3, 3), "algorithmic_bytes": fb, "achieved_GBs": round(f_gbs, 1),
