@@ -314,6 +314,35 @@ def test_device_entry_points_validate_before_launching():
     assert L.svdq_act_absmax_update_device(a, 0, 64, a, None) == 0   # empty batch: nothing to launch
 
 
+def test_fused_plan_and_its_debug_entry_point_validate():
+    """svdq_forward_fused (host only) takes small layers and refuses the rest; the fused
+    debug launch rejects bad arguments before any HIP call (nothing here has a GPU).  The
+    work bound assumes the MI355X's 256 compute units, which is also the count the library
+    assumes where it cannot query a device."""
+    L = S._lib
+    fused = lambda M, K, N, r: S.svdq_forward_fused(M, K, N, r)
+    assert fused(1024, 640, 640, 32)          # 100 blocks of 16 x 16 x 64 per compute unit
+    assert fused(256, 1024, 1024, 16)
+    assert fused(1, 64, 16, 16)
+    assert fused(37, 1280, 2560, 32)
+    assert not fused(4096, 640, 640, 32)      # 400 per compute unit: the two kernels
+    assert not fused(1024, 1280, 1280, 32)
+    assert not fused(256, 1344, 256, 16)      # K past 1280
+    assert not fused(256, 640, 640, 48)       # r past 32
+    assert not fused(256, 640, 2576, 16)      # N past 2560
+    assert not fused(0, 640, 640, 16) and not fused(256, 600, 640, 16) and not fused(256, 640, 600, 16)
+    a = 1 << 20
+    dbg = lambda M=256, K=1024, N=1024, r=16, qx=a, sx=a, act=0, X=a: L.svdq_debug_fused_forward(
+        X, M, K, N, r, a, a, a, a, a, a, act, a, qx, sx, None)
+    assert dbg(M=4096, K=640, N=640, r=32) == 1
+    assert "fused" in S.svdq_last_error()
+    assert dbg(qx=None) == 1
+    assert dbg(sx=None) == 1
+    assert dbg(act=5) == 1
+    assert dbg(X=a + 4) == 3
+    assert dbg(qx=a + 8) == 3
+
+
 def test_append_lora_bit_exact_with_oracle():
     """The library's LoRA concatenation gives the oracle's bytes (one rounding of
     A[k, j] s[k] and of B[j, n] to bf16)."""

@@ -105,3 +105,18 @@ def test_mxfp4_entry_points_check_the_k_tiled_scales():
     with pytest.raises(ValueError, match="sx_e8m0 must have shape"):
         S.svdq_quantize_activations_mxfp4(d["X"], d["s"], d["L1"], g((M, Kx // 2), torch.uint8),
                                           g((M, Kx // 64), torch.uint8), g((M, r), torch.float32))
+
+
+@pytest.mark.parametrize("key,bad,msg", [
+    ("qx", g((M, K), torch.uint8), "qx must have shape"),
+    ("sx", g((M, K // 32), torch.float32), "sx must have shape"),
+    ("sx", g((M, K // 64), torch.float64), "sx must have dtype"),
+    ("Y", g((M, N - 16), torch.int16), "Y must have shape"),
+    ("qx", g((M, K // 2), torch.uint8, "cuda:1"), "different devices"),
+])
+def test_fused_debug_entry_rejects_mismatched_tensors(key, bad, msg):
+    d = layer(qx=g((M, K // 2), torch.uint8), sx=g((M, K // 64), torch.float32))
+    d[key] = bad
+    with pytest.raises(ValueError, match=msg):
+        S.svdq_debug_fused_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"],
+                                   S.SVDQ_ACT_NONE, d["Y"], d["qx"], d["sx"])
