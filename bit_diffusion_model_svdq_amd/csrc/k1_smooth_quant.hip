@@ -213,24 +213,8 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       for (int b = 0; b < 2; ++b) {
         am[b] = fmaxf(am[b], __shfl_xor(am[b], 16));
         am[b] = fmaxf(am[b], __shfl_xor(am[b], 32));
-        const int ef = (int)((__float_as_uint(am[b]) >> 23) & 0xFFu);
-        bytes[b] = (uint32_t)max(ef - 2, 0);
-        const float* v = xh + 8 * b;
-        float sc = __uint_as_float(bytes[b] << 23);            // 2^(byte - 127)
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = v[i];
-        if (bytes[b] == 0u) {                                   // 2^-127 is not a normal float
-          sc = 1.0f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = v[i] * 0x1p127f;   // exact: |v| < 2^-125
-        }
-        uint32_t w = 0u;
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], sc, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], sc, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], sc, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], sc, 3);
-        words[b] = w;
+        bytes[b] = quant::mx_scale_byte(am[b]);
+        words[b] = quant::mx_codes8(xh + 8 * b, bytes[b]);
       }
       codes.x = words[0];
       codes.y = words[1];

@@ -246,11 +246,76 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
     copy_step(sb + min(1, nsteps - 1), ring1);
     if (NR == 4) copy_step(sb + min(2, nsteps - 1), ring2);
   };
-  if (MODE == kWhole)
+  if (MODE == kWhole && r >= 16 && r <= 32 && t_slices <= 2) {
+    // One chunk of ranks and at most two T slices (every rank of the usual
+    // layers): the same arithmetic as tail::lowrank_bias_add, but its loads
+    // leave before the first copies and the wait for them leaves the copies
+    // in flight, so the branch's MFMAs run under the copies' latency.  (The
+    // general routine's runtime loops over rank chunks and slices make the
+    // compiler wait for every load in flight.)
+    const int jc = min(8 * fk, r - 8);
+    const bool j_ok = 8 * fk < r;
+    const long s1 = t_slices > 1 ? t_stride : 0;
+    float4 ta[C::TM], tb[C::TM], ua[C::TM], ub[C::TM];
+    uint4 lf[C::TN];
+#pragma unroll
+    for (int t = 0; t < C::TM; ++t) {
+      const float* tr = T + (size_t)min(m0 + wr + 16 * t + fr, M - 1) * r + jc;
+      ta[t] = *reinterpret_cast<const float4*>(tr);
+      tb[t] = *reinterpret_cast<const float4*>(tr + 4);
+      ua[t] = *reinterpret_cast<const float4*>(tr + s1);
+      ub[t] = *reinterpret_cast<const float4*>(tr + s1 + 4);
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+      lf[tn] = *reinterpret_cast<const uint4*>(L2 + (size_t)min(n0 + wc + 16 * tn + fr, N - 1) * r + jc);
+    __builtin_amdgcn_sched_barrier(0);   // the branch's loads leave first,
+    first_copies();
+    __builtin_amdgcn_sched_barrier(0);   // then the copies,
+    wait_vmcnt<C::CPW * (NR - 1)>();     // and the wait leaves only the copies in flight
+    __builtin_amdgcn_sched_barrier(0);
+    // the second slice's sum, unconditional so that its loads stay ahead of
+    // the copies (in a branch the compiler moves them behind the wait);
+    // with one slice it adds -0, which leaves every value as it is
+    const bool two = t_slices > 1;
+    const float4 nz = make_float4(-0.f, -0.f, -0.f, -0.f);
+#pragma unroll
+    for (int t = 0; t < C::TM; ++t) {
+      ta[t] = tail::add4(ta[t], two ? ua[t] : nz);
+      tb[t] = tail::add4(tb[t], two ? ub[t] : nz);
+    }
+    // ranks past r are zeroed by a bit mask (+0, as a select would give): a
+    // select on a loaded value may become a load under a lane mask, behind
+    // the wait
+    const uint32_t jm = j_ok ? 0xFFFFFFFFu : 0u;
+    tail::bf16x8 thi[C::TM], tlo[C::TM];
+#pragma unroll
+    for (int t = 0; t < C::TM; ++t) {
+      const float tv[8] = {ta[t].x, ta[t].y, ta[t].z, ta[t].w, tb[t].x, tb[t].y, tb[t].z, tb[t].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = __uint_as_float(__float_as_uint(tv[e]) & jm);
+        const __bf16 h = (__bf16)v;
+        thi[t][e] = h;
+        tlo[t][e] = (__bf16)(v - (float)h);
+      }
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const tail::bf16x8 l =
+          tail::as_bf16x8(make_uint4(lf[tn].x & jm, lf[tn].y & jm, lf[tn].z & jm, lf[tn].w & jm));
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) {
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(thi[tm], l, acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tlo[tm], l, acc[tm][tn], 0, 0, 0);
+      }
+    }
+  } else if (MODE == kWhole) {
     tail::lowrank_bias_add<C::TM, C::TN, 0>(acc, T, t_slices, t_stride, r, L2, nullptr, m0, n0, M,
                                             N, wr, wc, lane, 1.0f, first_copies);
-  else
+  } else {
     first_copies();
+  }
   // whole turns of the ring without branches (so that the compiler's count of
   // the copies in flight stays exact), then the last 0..3 steps
   int j0 = 0;

@@ -1,6 +1,6 @@
-// The int4 activation quantizer's arithmetic, shared by every kernel that
-// produces activation codes (the standalone quantize kernel and the fused
-// small-K forward), so that their codes and scales agree bit for bit.
+// The activation quantizers' arithmetic (int4 and MXFP4), shared by every
+// kernel that produces activation codes (the standalone quantize kernel and
+// the fused small-K forwards), so that their codes and scales agree bit for bit.
 //
 // SVDQuant (Terminology Entry, section 2.3, equations E2-E4): the smoothed
 // activation x_hat = x * fl32(1 / s) is cut into groups of 64 channels along
@@ -56,6 +56,40 @@ __device__ inline uint32_t pack8(const float* z) {
   const uint32_t b0 = nib2(z[0], z[1]), b1 = nib2(z[2], z[3]);
   const uint32_t b2 = nib2(z[4], z[5]), b3 = nib2(z[6], z[7]);
   return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+}
+
+// MXFP4 (the OCP microscaling format): a block of 32 channels shares one E8M0
+// scale byte, 2^(byte - 127), with byte = max(exponent field of the block
+// absmax - 2, 0), i.e. the shared exponent floor(log2 amax) - 2 clamped at
+// -127; each value becomes an FP4 E2M1 code of value / scale, rounded to
+// nearest even with saturation at +-6, the sign kept for a value that rounds
+// to zero.
+__device__ inline uint32_t mx_scale_byte(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)(ef - 2 > 0 ? ef - 2 : 0);
+}
+
+// 8 values of one block under its scale byte -> 8 FP4 codes in one dword
+// (channel 2i in the low nibble of byte i).  v_cvt_scalef32_pk_fp4_f32 divides
+// by the power-of-two scale and rounds, two values per instruction.  A block
+// whose scale would be the subnormal 2^-127 (byte 0: absmax < 2^-125) is
+// converted as v * 2^127 with scale 1 instead, which is exact.
+__device__ inline uint32_t mx_codes8(const float* v, uint32_t byte) {
+  float sc = __uint_as_float(byte << 23);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v[i];
+  if (byte == 0u) {
+    sc = 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = v[i] * 0x1p127f;
+  }
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], sc, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], sc, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], sc, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], sc, 3);
+  return w;
 }
 
 }  // namespace quant
