@@ -231,12 +231,13 @@ def main():
     quantize = S.svdq_forward_quantize_mxfp4 if mx else S.svdq_forward_quantize
     gemm = S.svdq_forward_gemm_mxfp4 if mx else S.svdq_forward_gemm
 
-    # narrow int4 layers run as one fused kernel: the step is then the forward call itself
-    fused = (not mx) and args.path == "auto" and S.svdq_forward_fused(M, K, N, r)
+    # narrow layers run as one fused kernel: the step is then the forward call itself
+    fused = args.path == "auto" and (S.svdq_forward_fused_mxfp4 if mx else S.svdq_forward_fused)(M, K, N, r)
+    forward = S.svdq_linear_forward_mxfp4 if mx else S.svdq_linear_forward
 
     def step(d):
         if fused:
-            S.svdq_linear_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"])
+            forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"])
         else:
             quantize(d["X"], d["s"], d["L1"], d["work"])
             gemm(M, K, d["L2"], d["Wq"], d["ws"], d["b"], d["Y"], d["work"], r)
@@ -378,20 +379,21 @@ def main():
     }
 
     if fused:   # one kernel: it is the dominant one, and k1/k2 do not run
-        fb = (M * K * 2 + N * K // 2 + N * (K // 64) * 4 + r * K * 2 + N * r * 2 + K * 4 + 2 * N
+        fb = (M * K * 2 + N * K // 2 + N * sb_row + r * K * 2 + N * r * 2 + K * 4 + 2 * N
               + M * N * 2)
+        fkern = "mxfp4_fused_smallk" if mx else "w4a4_fused_smallk"
         f_bound = "mfma" if ops_main / (peak_mfma * 1e12) >= fb / (PEAK_HBM_GBS * 1e9) else "hbm"
         f_gbs = fb / (k1_ms * 1e-3) / 1e9
         f_tops = ops_main / (k1_ms * 1e-3) / 1e12
         f_ach, f_peak, f_unit = (f_tops, peak_mfma, "TFLOP/s") if f_bound == "mfma" else \
             (f_gbs, PEAK_HBM_GBS, "GB/s")
         out["roofline"] = {
-            "kernel": "w4a4_fused_smallk (quantize + lora_down + GEMM + lora_up in one kernel)",
+            "kernel": f"{fkern} (quantize + lora_down + GEMM + lora_up in one kernel)",
             "bound": f_bound, "achieved": round(f_ach, 2), "peak": f_peak, "unit": f_unit,
             "frac": round(f_ach / f_peak, 4), "algorithmic": {"ops": ops_main, "bytes": fb},
             "traffic": load_traffic("k12_fused_smallk.hip", tkey),
             "avg_launch_us": round(k1_ms * 1e3, 3)}
-        out["kernels"] = {"w4a4_fused_smallk": {
+        out["kernels"] = {fkern: {
             "avg_launch_us": round(k1_ms * 1e3, 3), "algorithmic_bytes": fb, "achieved_GBs": round(f_gbs, 1),
             "peak_GBs": PEAK_HBM_GBS, "frac_hbm": round(f_gbs / PEAK_HBM_GBS, 4), "ops": ops_main,
             "achieved_TOPS": round(f_tops, 2), "pct_mfma_peak": round(100.0 * f_tops / peak_mfma, 2)}}

@@ -51,7 +51,8 @@ EXPORTS = [
     "svdq_forward_gemm_act_mxfp4", "svdq_mxfp4_tiled_scale_bytes", "svdq_mxfp4_tile_scales",
     "svdq_act_absmax_update_device", "svdq_forward_workspace_layout",
     "svdq_forward_workspace_layout_mxfp4", "svdq_static_workspace_bytes", "svdq_linear_forward_noalloc",
-    "svdq_forward_fused", "svdq_debug_fused_forward",
+    "svdq_forward_fused", "svdq_debug_fused_forward", "svdq_forward_fused_mxfp4",
+    "svdq_debug_fused_forward_mxfp4",
 ]
 
 # svdq_activation
@@ -89,6 +90,8 @@ _sig = {
     "svdq_static_workspace_bytes": [],
     "svdq_forward_fused": [_I, _I, _I, _I],
     "svdq_debug_fused_forward": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P],
+    "svdq_forward_fused_mxfp4": [_I, _I, _I, _I],
+    "svdq_debug_fused_forward_mxfp4": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P],
     "svdq_linear_forward_noalloc": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P],
     "svdq_forward_workspace_layout_mxfp4": [_I, _I, _I, _I, _P, _P, _P, _P, _P],
     "svdq_quantize_residual_mxfp4": [_P, _I, _I, _P, _P, _P, _I, _P, _P],
@@ -419,6 +422,28 @@ def svdq_debug_fused_forward(X, smooth, L1, L2, Wq, w_scales, bias, activation, 
                                        _dp(w_scales), _dp(bias), int(activation), _dp(Y), _dp(qx), _dp(sx),
                                        _stream(stream))
     _check(st, "svdq_debug_fused_forward")
+    return Y
+
+
+def svdq_forward_fused_mxfp4(M, K, N, r) -> bool:
+    """Whether the MXFP4 forward runs (M, K, N, r) as the single fused small-K kernel."""
+    return bool(_lib.svdq_forward_fused_mxfp4(int(M), int(K), int(N), int(r)))
+
+
+def svdq_debug_fused_forward_mxfp4(X, smooth, L1, L2, Wq, w_e8m0, bias, activation, Y, qx, sx_e8m0,
+                                   stream=None):
+    """The fused MXFP4 forward, also writing its codes qx [M, K/2] and E8M0 bytes sx_e8m0 [M, K/32]."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    r = _rank_of(L1, L2)
+    _check_layer(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y, mx=True)
+    _need(qx, "qx", ("uint8",), (M, K // 2))
+    _need(sx_e8m0, "sx_e8m0", ("uint8",), (M, K // 32))
+    _same_device(X, qx, sx_e8m0)
+    st = _lib.svdq_debug_fused_forward_mxfp4(_dp(X), M, K, N, r, _dp(smooth), _dp(L1), _dp(L2), _dp(Wq),
+                                             _dp(w_e8m0), _dp(bias), int(activation), _dp(Y), _dp(qx),
+                                             _dp(sx_e8m0), _stream(stream))
+    _check(st, "svdq_debug_fused_forward_mxfp4")
     return Y
 
 

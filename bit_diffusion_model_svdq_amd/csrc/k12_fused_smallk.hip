@@ -419,6 +419,312 @@ hipError_t launch_nt(const uint16_t* X, int M, int K, int N, int r, const float*
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ MXFP4
+// The same forward with Q taken as MXFP4: E2M1 codes with one E8M0 scale per
+// 32 channels, multiplied by v_mfma_scale_f32_16x16x128_f8f6f4, which applies
+// both blocks' scales itself (lane l supplies row or column l % 16, channels
+// 32 (l / 16) .. + 31 of a 128-channel step, canonical packed, and that
+// block's scale byte).  So a quantizer lane owns one whole block of one row:
+// the absmax is lane-local, and its 16 code bytes and scale byte are exactly
+// its A operand of the step; W is read 16 bytes per lane in the same layout,
+// with no exchange between lanes; and there is no per-group epilogue.  The
+// quantizer is quant_core.h's (the standalone quantize kernel's), T uses the
+// same bf16 hi/lo MFMAs over four 8-channel chunks of the lane's block.
+constexpr int kMxStep = 128;   // channels per block-scaled MFMA
+constexpr int kFmtFp4 = 4;     // cbsz / blgp code of FP4 E2M1
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// LDS: inv_s [K] f32 | afrag [S][64 lanes] 16 B | sxl [S][64] i32 (scale bytes)
+// | tfin [16][r] f32 | sws [ceil(S/2)][bn][8] bytes (weight scales, k-tiled as
+// in global memory) | bias [bn] f32 | scratch: the waves' partial T
+// [8][16][r] f32, later the output tile [16][bn] bf16.
+__host__ __device__ inline FusedLds fused_lds_mx(int K, int r, int bn) {
+  const int S = K / kMxStep;
+  FusedLds l;
+  l.inv_s = 0;
+  l.afrag = K * 4;
+  l.sxl = l.afrag + S * 1024;
+  l.tfin = l.sxl + S * 256;
+  l.sws = l.tfin + 16 * r * 4;
+  l.bias = l.sws + (S + 1) / 2 * bn * 8;
+  l.scratch = l.bias + bn * 4;
+  const int tpart = kFW * 16 * r * 4, out = 16 * bn * 2;
+  l.bytes = l.scratch + (tpart > out ? tpart : out);
+  return l;
+}
+
+// NT: column tiles of 16 per wave; NS: 128-channel steps a wave quantizes at
+// most (ceil(S / 8): 1 up to K = 1024, 2 up to K = 1280).
+template <int NT, int NS>
+__global__ __launch_bounds__(kFThreads, 1) void mxfp4_fused_smallk_kernel(
+    const uint16_t* __restrict__ X, int M, int K, const float* __restrict__ smooth,
+    const uint16_t* __restrict__ L1, int r, const uint16_t* __restrict__ L2,
+    const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ w_e8m0,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int N, int act,
+    uint8_t* __restrict__ dbg_qx, uint8_t* __restrict__ dbg_sx) {
+  constexpr int BN = 16 * NT * kFW;
+  constexpr int RTMAX = kFusedMaxRank / 16;
+  constexpr int T2MAX = (kFusedMaxK / kMxStep + 1) / 2;
+  constexpr int SWPER = (T2MAX * BN + kFThreads - 1) / kFThreads;   // 8-byte scale rows per thread
+  constexpr int BPER = (BN + kFThreads - 1) / kFThreads;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const FusedLds LL = fused_lds_mx(K, r, BN);
+  float* inv_s = reinterpret_cast<float*>(lds + LL.inv_s);
+  uint4* afrag = reinterpret_cast<uint4*>(lds + LL.afrag);
+  int* sxl = reinterpret_cast<int*>(lds + LL.sxl);
+  float* tfin = reinterpret_cast<float*>(lds + LL.tfin);
+  uint8_t* sws = lds + LL.sws;
+  float* bias_l = reinterpret_cast<float*>(lds + LL.bias);
+  float* tpart = reinterpret_cast<float*>(lds + LL.scratch);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15;
+  const int fk = lane >> 4;
+  const int S = K / kMxStep;
+  const int T2 = (S + 1) / 2;
+  const int KB = K / 2;
+  const int RT = r / 16;
+  const int m0 = blockIdx.x * 16;
+  const int n0 = blockIdx.y * BN;
+  const int wc = wave * 16 * NT;
+  const int row = min(m0 + fr, M - 1);     // rows past M quantize a valid row, never stored
+
+  // ---- 1. loads, in order of use (as in the int4 kernel: unconditional,
+  // clamped, so that none waits behind a branch)
+  constexpr int kSPer = kFusedMaxK / kFThreads + 1;
+  float sv[kSPer];
+#pragma unroll
+  for (int i = 0; i < kSPer; ++i) sv[i] = smooth[min(tid + i * kFThreads, K - 1)];
+  const int ns = wave < S ? (S - wave + kFW - 1) / kFW : 0;   // steps this wave quantizes (<= NS)
+  uint4 xv[NS][4], lv[NS][RTMAX][4];
+  const uint16_t* xrow = X + (size_t)row * K + 32 * fk;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int st = min(wave + kFW * i, S - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[i][q] = *reinterpret_cast<const uint4*>(xrow + st * kMxStep + 8 * q);
+  }
+  const uint16_t* l1b = r > 0 ? L1 : X;                      // a valid dummy for r = 0
+  const int l1k = r > 0 ? K : 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int st = min(wave + kFW * i, S - 1);
+#pragma unroll
+    for (int j = 0; j < RTMAX; ++j) {
+      const uint16_t* lp = l1b + (size_t)min(16 * j + fr, max(r, 1) - 1) * l1k + (r > 0 ? st * kMxStep + 32 * fk : 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lv[i][j][q] = *reinterpret_cast<const uint4*>(lp + 8 * q);
+    }
+  }
+  // the workgroup's weight scales: k-tiled [T2][N][8], rows n0 .. n0 + BN - 1
+  // of each tile one contiguous run (rows past N: the last row)
+  const int nsw = T2 * BN;
+  uint2 swr[SWPER];
+#pragma unroll
+  for (int i = 0; i < SWPER; ++i) {
+    const int e = min(tid + i * kFThreads, nsw - 1);
+    const int t = e / BN;
+    swr[i] = *reinterpret_cast<const uint2*>(w_e8m0 + ((size_t)t * N + min(n0 + e - t * BN, N - 1)) * 8);
+  }
+  const uint16_t* bb = bias ? bias : X;
+  uint16_t brr[BPER];
+#pragma unroll
+  for (int i = 0; i < BPER; ++i) brr[i] = bb[bias ? min(n0 + min(tid + i * kFThreads, BN - 1), N - 1) : 0];
+  int ncol[NT];
+#pragma unroll
+  for (int tn = 0; tn < NT; ++tn) ncol[tn] = min(n0 + wc + 16 * tn + fr, N - 1);
+  const uint16_t* l2b = r > 0 ? L2 : X;
+  const int jq = min(8 * fk, max(r, 8) - 8);                  // ranks 8 fk .. + 7 of the one chunk
+  uint4 l2v[NT];
+#pragma unroll
+  for (int tn = 0; tn < NT; ++tn) l2v[tn] = *reinterpret_cast<const uint4*>(l2b + (r > 0 ? (size_t)ncol[tn] * r + jq : 0));
+
+  // W, 16 bytes per lane: step st, bytes 16 fk of its 64 (past the last step: clamped)
+  const uint8_t* wrow[NT];
+#pragma unroll
+  for (int tn = 0; tn < NT; ++tn) wrow[tn] = Wq + (size_t)ncol[tn] * KB + 16 * fk;
+  uint4 wring[kDepth][NT];
+  auto load_w = [&](int slot, int st) {
+    const int off = min(st, S - 1) * (kMxStep / 2);
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn) wring[slot][tn] = *reinterpret_cast<const uint4*>(wrow[tn] + off);
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load_w(d, d);
+
+  // ---- 2. 1/s, the weight scales and the bias into LDS; then quantize and partial T
+#pragma unroll
+  for (int i = 0; i < kSPer; ++i) inv_s[min(tid + i * kFThreads, K - 1)] = 1.0f / sv[i];  // duplicates equal
+#pragma unroll
+  for (int i = 0; i < SWPER; ++i) {
+    const int e = tid + i * kFThreads;
+    if (e < nsw) *reinterpret_cast<uint2*>(sws + 8 * e) = swr[i];   // [t][column][8]
+  }
+#pragma unroll
+  for (int i = 0; i < BPER; ++i)
+    if (tid + i * kFThreads < BN) bias_l[tid + i * kFThreads] = bias ? __uint_as_float(uint32_t(brr[i]) << 16) : 0.f;
+  lds_barrier();
+
+  f32x4 at[RTMAX];
+#pragma unroll
+  for (int j = 0; j < RTMAX; ++j) at[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (i < ns) {
+      const int st = wave + kFW * i;
+      const uint32_t w[16] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w, xv[i][1].x, xv[i][1].y,
+                              xv[i][1].z, xv[i][1].w, xv[i][2].x, xv[i][2].y, xv[i][2].z, xv[i][2].w,
+                              xv[i][3].x, xv[i][3].y, xv[i][3].z, xv[i][3].w};
+      const float* is = inv_s + st * kMxStep + 32 * fk;
+      float xh[32];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        xh[2 * e] = __uint_as_float(w[e] << 16) * is[2 * e];
+        xh[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) * is[2 * e + 1];
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(xh[e]));
+      const uint32_t byte = quant::mx_scale_byte(amax);
+      const uint4 codes = make_uint4(quant::mx_codes8(xh, byte), quant::mx_codes8(xh + 8, byte),
+                                     quant::mx_codes8(xh + 16, byte), quant::mx_codes8(xh + 24, byte));
+      afrag[st * 64 + lane] = codes;
+      sxl[st * 64 + lane] = (int)byte;
+      if (dbg_qx && blockIdx.y == 0 && m0 + fr < M) {
+        *reinterpret_cast<uint4*>(dbg_qx + (size_t)(m0 + fr) * KB + st * (kMxStep / 2) + 16 * fk) = codes;
+        dbg_sx[(size_t)(m0 + fr) * (K / 32) + 4 * st + fk] = (uint8_t)byte;
+      }
+      // lora_down: x_hat as a bf16 hi/lo pair, four 8-channel chunks of the block
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = xh[8 * c + 2 * e], v1 = xh[8 * c + 2 * e + 1];
+          const uint32_t b0 = __float_as_uint(v0), b1 = __float_as_uint(v1);
+          hi[e] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+          lo[e] = cvt_bf16x2(v0 - __uint_as_float(b0 & 0xFFFF0000u), v1 - __uint_as_float(b1 & 0xFFFF0000u));
+        }
+        const bf16x8 ahi = bf16x8_of(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        const bf16x8 alo = bf16x8_of(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+        for (int j = 0; j < RTMAX; ++j) {
+          if (j < RT) {
+            const bf16x8 b = bf16x8_of(lv[i][j][c]);
+            at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, at[j], 0, 0, 0);
+            at[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, at[j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- 3. T = the waves' partials summed in wave order
+#pragma unroll
+  for (int j = 0; j < RTMAX; ++j)
+    if (j < RT)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tpart[(wave * 16 + 4 * fk + i) * r + 16 * j + fr] = at[j][i];
+  lds_barrier();
+  for (int e = tid; e < 16 * r; e += kFThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kFW; ++wv) s += tpart[wv * 16 * r + e];
+    tfin[e] = s;
+  }
+  lds_barrier();   // tfin, afrag and sxl are complete; tpart is free
+
+  // ---- 4. the GEMM over 128-channel steps, kDepth steps of W in flight; a
+  // step past the last (padding to whole turns) has zero A codes
+  f32x4 acc[1][NT];
+#pragma unroll
+  for (int tn = 0; tn < NT; ++tn) acc[0][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int Sp = (S + kDepth - 1) / kDepth * kDepth;
+  for (int s0 = 0; s0 < Sp; s0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      __builtin_amdgcn_sched_barrier(0);   // one slot's work at a time (see the int4 loop)
+      const int s = s0 + d;
+      uint4 wv[NT];
+#pragma unroll
+      for (int tn = 0; tn < NT; ++tn) wv[tn] = wring[d][tn];
+      load_w(d, s + kDepth);
+      const int sc = min(s, S - 1);
+      const uint32_t am = s < S ? 0xFFFFFFFFu : 0u;
+      const uint4 araw = afrag[sc * 64 + lane];
+      const v8i a = v8i{(int)(araw.x & am), (int)(araw.y & am), (int)(araw.z & am), (int)(araw.w & am), 0, 0, 0, 0};
+      const int sa = sxl[sc * 64 + lane];
+      const uint8_t* swp = sws + ((sc >> 1) * BN + wc + fr) * 8 + 4 * (sc & 1) + fk;
+#pragma unroll
+      for (int tn = 0; tn < NT; ++tn) {
+        const int sb = swp[16 * 8 * tn];
+        const v8i b = v8i{(int)wv[tn].x, (int)wv[tn].y, (int)wv[tn].z, (int)wv[tn].w, 0, 0, 0, 0};
+        acc[0][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[0][tn], kFmtFp4, kFmtFp4, 0,
+                                                                     sa, 0, sb);
+      }
+    }
+  }
+
+  // ---- 5. bias, T L2^T (r <= 32: one chunk of 32 ranks), activation, store
+#pragma unroll
+  for (int tn = 0; tn < NT; ++tn) {
+    const float bv = bias_l[wc + 16 * tn + fr];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][tn][i] += bv;
+  }
+  if (r > 0) {
+    const bool j_ok = 8 * fk < r;
+    const float* tp = tfin + fr * r + jq;
+    uint32_t thi[4], tlo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = j_ok ? tp[2 * e] : 0.f, v1 = j_ok ? tp[2 * e + 1] : 0.f;
+      const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+      thi[e] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+      tlo[e] = cvt_bf16x2(v0 - (float)h0, v1 - (float)h1);
+    }
+    const bf16x8 th = bf16x8_of(make_uint4(thi[0], thi[1], thi[2], thi[3]));
+    const bf16x8 tl = bf16x8_of(make_uint4(tlo[0], tlo[1], tlo[2], tlo[3]));
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn) {
+      const bf16x8 l = bf16x8_of(j_ok ? l2v[tn] : make_uint4(0u, 0u, 0u, 0u));
+      acc[0][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, l, acc[0][tn], 0, 0, 0);
+      acc[0][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, l, acc[0][tn], 0, 0, 0);
+    }
+  }
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds + LL.scratch);
+  tail::store_tile<1, NT, 16, BN, kFThreads>(acc, nullptr, Y, N, m0, n0, M, N, 0, wc, lane, tid,
+                                             [&](int rr) { return otile + rr * BN; }, act);
+}
+
+template <int NT, int NS>
+hipError_t allow_lds_mx() {
+  static std::atomic<bool> done{false};
+  if (done.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mxfp4_fused_smallk_kernel<NT, NS>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
+  return e;
+}
+
+template <int NT, int NS>
+hipError_t launch_nt_mx(const uint16_t* X, int M, int K, int N, int r, const float* smooth,
+                        const uint16_t* L1, const uint16_t* L2, const uint8_t* Wq,
+                        const uint8_t* w_e8m0, const uint16_t* bias, uint16_t* Y, int act,
+                        uint8_t* dbg_qx, uint8_t* dbg_sx, hipStream_t stream) {
+  constexpr int BN = 16 * NT * kFW;
+  const FusedLds l = fused_lds_mx(K, r, BN);
+  const hipError_t e = allow_lds_mx<NT, NS>();
+  if (e != hipSuccess) return e;
+  const dim3 grid((M + 15) / 16, (N + BN - 1) / BN);
+  hipLaunchKernelGGL((mxfp4_fused_smallk_kernel<NT, NS>), grid, dim3(kFThreads), l.bytes, stream, X, M,
+                     K, smooth, L1, r, L2, Wq, w_e8m0, bias, Y, N, act, dbg_qx, dbg_sx);
+  return hipGetLastError();
+}
+
+
 }  // namespace
 
 FusedPlan fused_plan(int M, int K, int N, int r) {
@@ -468,6 +774,35 @@ hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, 
     default: return hipErrorInvalidValue;
   }
 #undef SVDQ_FUSED_CASE
+}
+
+FusedPlan fused_plan_mx(int M, int K, int N, int r) {
+  FusedPlan p;
+  if (K % kMxStep != 0) return p;
+  return fused_plan(M, K, N, r);
+}
+
+hipError_t launch_fused_smallk_mx(const FusedPlan& plan, const uint16_t* X, int M, int K, int N, int r,
+                                  const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                  const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
+                                  uint16_t* Y, int act, uint8_t* dbg_qx, uint8_t* dbg_sx,
+                                  hipStream_t stream) {
+  const bool two = K > kFW * kMxStep;   // more than 8 steps: some waves quantize two
+#define SVDQ_FUSED_MX_CASE(nt)                                                                          \
+  case nt:                                                                                               \
+    return two ? launch_nt_mx<nt, 2>(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y, act, dbg_qx,    \
+                                     dbg_sx, stream)                                                     \
+               : launch_nt_mx<nt, 1>(X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y, act, dbg_qx,    \
+                                     dbg_sx, stream);
+  switch (plan.nt) {
+    SVDQ_FUSED_MX_CASE(1)
+    SVDQ_FUSED_MX_CASE(2)
+    SVDQ_FUSED_MX_CASE(3)
+    SVDQ_FUSED_MX_CASE(4)
+    SVDQ_FUSED_MX_CASE(5)
+    default: return hipErrorInvalidValue;
+  }
+#undef SVDQ_FUSED_MX_CASE
 }
 
 }  // namespace svdq

@@ -250,6 +250,11 @@ svdq_status linear_forward_mx(const uint16_t* X, int M, int K, int N, int r, con
   if (workspace_bytes < w.bytes)
     return fail(SVDQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const FusedPlan fp = fused_plan_mx(M, K, N, r);
+  if (fp.use)
+    return hip_check(launch_fused_smallk_mx(fp, X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y,
+                                            act, nullptr, nullptr, s),
+                     "fused small-K forward (MXFP4) launch");
   SVDQ_TRY(hip_check(launch_smooth_quant_lora_down_mx(X, M, K, r, smooth, L1, w.qx, w.sx, w.T,
                                                       false, w.sx_rows, s),
                      "smooth_quant_lora_down (MXFP4) launch"));
@@ -480,6 +485,34 @@ svdq_status svdq_debug_fused_forward(const uint16_t* X, int M, int K, int N, int
     return hip_check(launch_fused_smallk(fp, X, M, K, N, r, smooth, L1, L2, Wq, w_scales, bias, Y,
                                          activation, qx, sx, static_cast<hipStream_t>(stream)),
                      "fused small-K forward launch");
+  });
+}
+
+int svdq_forward_fused_mxfp4(int M, int K, int N, int r) {
+  if (M < 1 || K < 128 || K % 128 || N < 16 || N % 16 || r < 0 || r > kMaxRank || r % 16) return 0;
+  return fused_plan_mx(M, K, N, r).use ? 1 : 0;
+}
+
+svdq_status svdq_debug_fused_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                           const float* smooth, const uint16_t* L1,
+                                           const uint16_t* L2, const uint8_t* Wq,
+                                           const uint8_t* w_e8m0, const uint16_t* bias,
+                                           int activation, uint16_t* Y, uint8_t* qx,
+                                           uint8_t* sx_e8m0, void* stream) {
+  return guarded([&]() -> svdq_status {
+    SVDQ_TRY(check_shapes_mx(M, K, N, r));
+    SVDQ_TRY(stage1_checks(X, M, K, r, smooth, L1));
+    SVDQ_TRY(stage2_checks(r, L2, Wq, reinterpret_cast<const float*>(w_e8m0), bias, Y));
+    SVDQ_TRY(check_act(activation));
+    SVDQ_TRY(check_ptr(qx, "qx", false));
+    SVDQ_TRY(check_ptr(sx_e8m0, "sx_e8m0", false));
+    const FusedPlan fp = fused_plan_mx(M, K, N, r);
+    if (!fp.use)
+      return fail(SVDQ_ERR_INVALID_ARG, "M=%d K=%d N=%d r=%d does not take the fused small-K path", M, K,
+                  N, r);
+    return hip_check(launch_fused_smallk_mx(fp, X, M, K, N, r, smooth, L1, L2, Wq, w_e8m0, bias, Y,
+                                            activation, qx, sx_e8m0, static_cast<hipStream_t>(stream)),
+                     "fused small-K forward (MXFP4) launch");
   });
 }
 

@@ -135,6 +135,17 @@ hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, 
                                uint16_t* Y, int act, uint8_t* dbg_qx, float* dbg_sx,
                                hipStream_t stream);
 
+// The fused small-K forward with MXFP4 (E2M1 codes, E8M0 scales per 32
+// channels; w_e8m0 k-tiled): the same range, with K a multiple of 128.
+// dbg_qx / dbg_sx (both NULL, or both set): the codes ([M, K/2] packed) and
+// the scale bytes ([M, K/32], row-major), written by the first column slice.
+FusedPlan fused_plan_mx(int M, int K, int N, int r);
+hipError_t launch_fused_smallk_mx(const FusedPlan& plan, const uint16_t* X, int M, int K, int N, int r,
+                                  const float* smooth, const uint16_t* L1, const uint16_t* L2,
+                                  const uint8_t* Wq, const uint8_t* w_e8m0, const uint16_t* bias,
+                                  uint16_t* Y, int act, uint8_t* dbg_qx, uint8_t* dbg_sx,
+                                  hipStream_t stream);
+
 // k2's main loop with the integer group partials exported instead of the epilogue.
 hipError_t launch_group_partials(const uint8_t* qx, const uint8_t* Wq, int M, int N, int K,
                                  int m0, int m1, int n0, int n1, int32_t* P, hipStream_t stream);

@@ -305,7 +305,9 @@ svdq_status svdq_forward_workspace_layout_mxfp4(int M, int K, int N, int r, size
 /* The MXFP4 forward: quantize + lora_down, then the block-scaled GEMM whose
  * epilogue adds the lora_up product and the bias.  w_e8m0 is k-tiled
  * [ceil(K/256)][N][8] (see above); the workspace holds the activation scales
- * k-tiled too.  Device memory, asynchronous on `stream`, no allocation. */
+ * k-tiled too.  Small layers (svdq_forward_fused_mxfp4 != 0) run as one fused
+ * kernel, as the int4 forward does, and leave the workspace untouched.
+ * Device memory, asynchronous on `stream`, no allocation. */
 svdq_status svdq_linear_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
                                       const float* smooth, const uint16_t* L1,
                                       const uint16_t* L2, const uint8_t* Wq,
@@ -333,6 +335,24 @@ svdq_status svdq_forward_gemm_act_mxfp4(int M, int K, int N, int r, const uint16
                                         const uint16_t* bias, int activation, uint16_t* Y,
                                         const void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/* 1 if the MXFP4 forward runs the shape as the single fused small-K kernel
+ * (the int4 range, with K a multiple of 128), else 0 (also for shapes the
+ * forward rejects).  Host only. */
+int svdq_forward_fused_mxfp4(int M, int K, int N, int r);
+
+/* The fused MXFP4 forward exactly as svdq_linear_forward_act_mxfp4 launches
+ * it, also writing the codes it quantized, qx [M, K/2] (canonical packed),
+ * and their E8M0 scale bytes sx_e8m0 [M, K/32] (row-major), as
+ * svdq_quantize_activations_mxfp4 writes them.  SVDQ_ERR_INVALID_ARG if
+ * svdq_forward_fused_mxfp4(M, K, N, r) is 0.  Device memory, asynchronous;
+ * the forward's own requirements otherwise (no workspace). */
+svdq_status svdq_debug_fused_forward_mxfp4(const uint16_t* X, int M, int K, int N, int r,
+                                           const float* smooth, const uint16_t* L1,
+                                           const uint16_t* L2, const uint8_t* Wq,
+                                           const uint8_t* w_e8m0, const uint16_t* bias,
+                                           int activation, uint16_t* Y, uint8_t* qx,
+                                           uint8_t* sx_e8m0, void* stream);
 
 /* Stage 1 into canonical buffers: qx [M, K/2], sx_e8m0 [M, K/32], T [M, r];
  * K <= 12544 as for svdq_quantize_activations. */

@@ -120,3 +120,25 @@ def test_fused_debug_entry_rejects_mismatched_tensors(key, bad, msg):
     with pytest.raises(ValueError, match=msg):
         S.svdq_debug_fused_forward(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"],
                                    S.SVDQ_ACT_NONE, d["Y"], d["qx"], d["sx"])
+
+
+def mx_layer(**over):
+    d = layer(Wq=g((N, K // 2), torch.uint8), ws=g((S.svdq_mxfp4_tiled_scale_bytes(N, K),), torch.uint8),
+              qx=g((M, K // 2), torch.uint8), sx=g((M, K // 32), torch.uint8))
+    d.update(over)
+    return d
+
+
+@pytest.mark.parametrize("key,bad,msg", [
+    ("qx", g((M, K // 4), torch.uint8), "qx must have shape"),
+    ("sx", g((M, K // 64), torch.uint8), "sx_e8m0 must have shape"),
+    ("sx", g((M, K // 32), torch.float32), "sx_e8m0 must have dtype"),
+    ("ws", g((N, K // 64), torch.uint8), "w_e8m0 must hold"),
+    ("sx", g((M, K // 32), torch.uint8, "cuda:1"), "different devices"),
+])
+def test_fused_mx_debug_entry_rejects_mismatched_tensors(key, bad, msg):
+    d = mx_layer()
+    d[key] = bad
+    with pytest.raises(ValueError, match=msg):
+        S.svdq_debug_fused_forward_mxfp4(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"],
+                                         S.SVDQ_ACT_NONE, d["Y"], d["qx"], d["sx"])
