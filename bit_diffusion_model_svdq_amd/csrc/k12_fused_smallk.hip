@@ -727,13 +727,17 @@ hipError_t launch_nt_mx(const uint16_t* X, int M, int K, int N, int r, const flo
 
 }  // namespace
 
-FusedPlan fused_plan(int M, int K, int N, int r) {
+namespace {
+
+// The plan of either format: used up to `per_cu` blocks of 16 x 16 outputs x
+// 64 channels per compute unit (past that, the two kernels are as fast).
+FusedPlan plan_for(int M, int K, int N, int r, long per_cu) {
   FusedPlan p;
   if (K > kFusedMaxK || r > kFusedMaxRank || N > kFusedMaxN || M < 1 || N < 16) return p;
   const int G = K / kGroup;
   const int cus = device_cu_count();
   const long group_tiles = (long)((M + 15) / 16) * (N / 16) * G;
-  if (group_tiles > 256L * cus) return p;   // past the crossover the two kernels are as fast
+  if (group_tiles > per_cu * cus) return p;
   const long row_blocks = (M + 15) / 16;
   // per-workgroup cost in group-tile units: the quantize phase (about four
   // tiles' worth per group a wave quantizes) plus the wave's GEMM over the
@@ -752,6 +756,10 @@ FusedPlan fused_plan(int M, int K, int N, int r) {
   p.use = true;
   return p;
 }
+
+}  // namespace
+
+FusedPlan fused_plan(int M, int K, int N, int r) { return plan_for(M, K, N, r, 256); }
 
 hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, int K, int N, int r,
                                const float* smooth, const uint16_t* L1, const uint16_t* L2,
@@ -776,10 +784,15 @@ hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, 
 #undef SVDQ_FUSED_CASE
 }
 
+// MXFP4 has no per-group epilogue, so its crossover lies further out where K
+// is short: measured against the two MXFP4 kernels, the fused kernel was
+// faster at 4096 x 640 -> 640 (400 blocks per compute unit; 14.8 against
+// 16.6 us) and slower at 6144 x 640 (600); at K = 1024 and 1280 it tied or
+// lost from about 256 on (1024 x 1024: 10.6 against 10.7 us; 768 x 1280,
+// 300: 15.9 against 13.5 us), as the int4 kernel does.
 FusedPlan fused_plan_mx(int M, int K, int N, int r) {
-  FusedPlan p;
-  if (K % kMxStep != 0) return p;
-  return fused_plan(M, K, N, r);
+  if (K % kMxStep != 0) return FusedPlan{};
+  return plan_for(M, K, N, r, K <= 640 ? 400 : 256);
 }
 
 hipError_t launch_fused_smallk_mx(const FusedPlan& plan, const uint16_t* X, int M, int K, int N, int r,

@@ -136,7 +136,8 @@ hipError_t launch_fused_smallk(const FusedPlan& plan, const uint16_t* X, int M, 
                                hipStream_t stream);
 
 // The fused small-K forward with MXFP4 (E2M1 codes, E8M0 scales per 32
-// channels; w_e8m0 k-tiled): the same range, with K a multiple of 128.
+// channels; w_e8m0 k-tiled): the same range with K a multiple of 128, and up
+// to 400 blocks per compute unit where K <= 640.
 // dbg_qx / dbg_sx (both NULL, or both set): the codes ([M, K/2] packed) and
 // the scale bytes ([M, K/32], row-major), written by the first column slice.
 FusedPlan fused_plan_mx(int M, int K, int N, int r);

@@ -337,8 +337,9 @@ svdq_status svdq_forward_gemm_act_mxfp4(int M, int K, int N, int r, const uint16
                                         void* stream);
 
 /* 1 if the MXFP4 forward runs the shape as the single fused small-K kernel
- * (the int4 range, with K a multiple of 128), else 0 (also for shapes the
- * forward rejects).  Host only. */
+ * (the int4 range, with K a multiple of 128, and up to 400 blocks of
+ * 16 x 16 outputs x 64 channels per compute unit where K <= 640), else 0
+ * (also for shapes the forward rejects).  Host only. */
 int svdq_forward_fused_mxfp4(int M, int K, int N, int r);
 
 /* The fused MXFP4 forward exactly as svdq_linear_forward_act_mxfp4 launches

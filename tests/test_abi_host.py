@@ -344,15 +344,18 @@ def test_fused_plan_and_its_debug_entry_point_validate():
 
 
 def test_fused_mx_plan_and_its_debug_entry_point_validate():
-    """svdq_forward_fused_mxfp4: the int4 range with K a multiple of 128; the MXFP4 fused
-    debug launch rejects bad arguments before any HIP call."""
+    """svdq_forward_fused_mxfp4: the int4 range with K a multiple of 128, and up to 400
+    blocks per compute unit where K <= 640; the MXFP4 fused debug launch rejects bad
+    arguments before any HIP call."""
     L = S._lib
     fused = lambda M, K, N, r: S.svdq_forward_fused_mxfp4(M, K, N, r)
     assert fused(1024, 640, 640, 32) and fused(256, 1024, 1024, 16) and fused(1, 128, 16, 16)
     assert fused(37, 1280, 2560, 32) and fused(300, 1280, 1280, 0)
     assert not fused(1, 64, 16, 16)           # K must be a multiple of 128
     assert not fused(256, 320, 640, 16)
-    assert not fused(4096, 640, 640, 32)      # 400 blocks per compute unit: the two kernels
+    assert fused(4096, 640, 640, 32)          # 400 blocks per compute unit at K = 640
+    assert not fused(6144, 640, 640, 32)      # 600: the two kernels
+    assert not fused(1024, 1280, 1280, 32)    # 400 at K = 1280: the two kernels
     assert not fused(256, 1408, 256, 16)      # K past 1280
     assert not fused(256, 640, 640, 48)       # r past 32
     assert not fused(256, 640, 2576, 16)      # N past 2560
@@ -360,7 +363,7 @@ def test_fused_mx_plan_and_its_debug_entry_point_validate():
     a = 1 << 20
     dbg = lambda M=256, K=1024, N=1024, r=16, qx=a, sx=a, act=0, X=a: L.svdq_debug_fused_forward_mxfp4(
         X, M, K, N, r, a, a, a, a, a, a, act, a, qx, sx, None)
-    assert dbg(M=4096, K=640, N=640, r=32) == 1
+    assert dbg(M=6144, K=640, N=640, r=32) == 1
     assert "fused" in S.svdq_last_error()
     assert dbg(K=320) == 1                    # not a multiple of 128
     assert dbg(qx=None) == 1

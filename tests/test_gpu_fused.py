@@ -128,7 +128,8 @@ def test_fused_range_and_rejection():
 
 # ---------------------------------------------------------------- MXFP4
 # The same fused forward with Q taken as MXFP4 (svdq_forward_fused_mxfp4: the
-# int4 range with K a multiple of 128): codes and E8M0 bytes bit-exact against
+# int4 range with K a multiple of 128, up to 400 blocks of 16 x 16 x 64 per
+# compute unit where K <= 640): codes and E8M0 bytes bit-exact against
 # the oracle's MXFP4 quantizer, every output within the MXFP4 forward tests'
 # tolerance of the oracle's forward_mx.
 from test_gpu_mxfp4 import check_y as check_y_mx  # noqa: E402
@@ -181,7 +182,7 @@ def check_codes_mx(p, qx, sx, label):
     np.testing.assert_array_equal(sx, sx_o, err_msg=f"{label}: E8M0 bytes")
 
 
-@pytest.mark.parametrize("name,M", [("smallk_640", 1024), ("smallk_1280", 256)])
+@pytest.mark.parametrize("name,M", [("smallk_640", 1024), ("smallk_640", None), ("smallk_1280", 256)])
 def test_fused_mx_smallk_workloads_codes_and_every_output(name, M):
     """The small-K UNet widths in MXFP4: codes and scale bytes bit-exact, every
     output within tolerance, the plain forward identical to the debug launch."""
@@ -228,7 +229,9 @@ def test_fused_mx_range_and_rejection():
     assert not S.svdq_forward_fused_mxfp4(1024, 1408, 640, 32)    # K past 1280
     assert not S.svdq_forward_fused_mxfp4(1024, 640, 640, 48)     # r past 32
     assert not S.svdq_forward_fused_mxfp4(1024, 640, 2576, 32)    # N past 2560
-    assert not S.svdq_forward_fused_mxfp4(4096, 640, 640, 32)     # 400 group-tiles per compute unit
+    assert not S.svdq_forward_fused_mxfp4(6144, 640, 640, 32)     # 600 group-tiles per compute unit
+    assert not S.svdq_forward_fused_mxfp4(1024, 1280, 1280, 32)   # 400 at K = 1280
+    assert S.svdq_forward_fused_mxfp4(4096, 640, 640, 32)         # 400 at K = 640
     assert S.svdq_forward_fused_mxfp4(1024, 640, 640, 32)
     p = mx_layer(64, 1408, 64, 16, seed=9)
     d = mx_device(p)

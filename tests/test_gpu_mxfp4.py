@@ -202,11 +202,16 @@ def forward_parts_mx(p):
     return d, ws
 
 
-def test_forward_mx_stages_match_fused_call():
+@pytest.mark.parametrize("name", ["smallk_1280", "smallk_640"])
+def test_forward_mx_stages_match_the_forward_call(name):
     """svdq_forward_quantize_mxfp4 then svdq_forward_gemm_mxfp4 (the workspace carries the
-    k-tiled activation scales between them) equal the fused call bit for bit."""
-    say("mx stages vs fused smallk_640")
-    p = packed_mx("smallk_640")
+    k-tiled activation scales between them) against svdq_linear_forward_mxfp4.  Where the
+    forward runs those two stages (1024 x 1280 -> 1280), the outputs are identical bit for
+    bit.  Where it runs the fused small-K kernel (4096 x 640 -> 640), that kernel sums T in
+    another order, so both results are held to the oracle instead (its codes and scale
+    bytes are compared bit for bit by the fused kernel's own tests)."""
+    say(f"mx stages vs forward {name}")
+    p = packed_mx(name)
     M, K, N, r = p["M"], p["K"], p["N"], p["r"]
     Yf = run_forward(p)
     d, ws = forward_parts_mx(p)
@@ -214,7 +219,13 @@ def test_forward_mx_stages_match_fused_call():
     S.svdq_forward_quantize_mxfp4(d["X"], d["s"], d["L1"], ws)
     S.svdq_forward_gemm_mxfp4(M, K, d["L2"], d["Wq"], d["we"], d["b"], Y, ws, r)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(O.bf16_to_f64(Y.cpu().numpy().view(np.uint16)), Yf)
+    Ys = O.bf16_to_f64(Y.cpu().numpy().view(np.uint16))
+    if not S.svdq_forward_fused_mxfp4(M, K, N, r):
+        np.testing.assert_array_equal(Ys, Yf)
+    else:
+        Yref = O.forward_mx(p["X"], p["s"], p["L1"], p["L2"], p["Wq"], p["we"], p["b"])
+        check_y(Ys, Yref, f"mx {name} two stages")
+        check_y(Yf, Yref, f"mx {name} fused forward")
 
 
 def test_forward_mx_in_hip_graph_replays_match_eager():
