@@ -246,13 +246,15 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
     copy_step(sb + min(1, nsteps - 1), ring1);
     if (NR == 4) copy_step(sb + min(2, nsteps - 1), ring2);
   };
-  if (MODE == kWhole && r >= 16 && r <= 32 && t_slices <= 2) {
+  if (MODE == kWhole && NR == 4 && r >= 16 && r <= 32 && t_slices <= 2) {
     // One chunk of ranks and at most two T slices (every rank of the usual
     // layers): the same arithmetic as tail::lowrank_bias_add, but its loads
     // leave before the first copies and the wait for them leaves the copies
     // in flight, so the branch's MFMAs run under the copies' latency.  (The
     // general routine's runtime loops over rank chunks and slices make the
-    // compiler wait for every load in flight.)
+    // compiler wait for every load in flight.)  Four-buffer rings only: with
+    // two workgroups per CU (the three-buffer ring) the other workgroup
+    // already covers the prologue, and there this head measured slower.
     const int jc = min(8 * fk, r - 8);
     const bool j_ok = 8 * fk < r;
     const long s1 = t_slices > 1 ? t_stride : 0;

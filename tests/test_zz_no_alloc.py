@@ -53,8 +53,12 @@ def both(p, act):
 def test_noalloc_forward_matches_workspace_forward_on_two_calls():
     assert S.svdq_static_workspace_bytes() == 64 << 20
     big = layer("dit_proj")                       # 4096 x 3072 -> 3072, r = 32: 8.1 MB of workspace
-    small = layer("tiny", M=200)                  # then 200 x 1024 -> 1024, r = 16, GELU
-    for p, act, tag in ((big, S.SVDQ_ACT_NONE, "dit_proj"), (small, S.SVDQ_ACT_GELU_TANH, "tiny 200 rows")):
+    # then the same layer on its first 1024 tokens with GELU: a smaller workspace in the
+    # same array (still the two-kernel forward, which uses it; small layers fuse and do not)
+    small = dict(big, X=big["X"][:1024])
+    M2, K2 = small["X"].shape
+    assert not S.svdq_forward_fused(M2, K2, small["Wq"].shape[0], small["L1"].shape[0])
+    for p, act, tag in ((big, S.SVDQ_ACT_NONE, "dit_proj"), (small, S.SVDQ_ACT_GELU_TANH, "dit_proj 1024 rows")):
         print(f"noalloc {tag}", flush=True)
         Yws, Yna = both(p, act)
         np.testing.assert_array_equal(Yna, Yws, err_msg=tag)
