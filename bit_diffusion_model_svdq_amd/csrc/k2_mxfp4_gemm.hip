@@ -100,6 +100,20 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// The wait before a barrier of the ring: vmcnt = n (this wave's copies of the
+// step have landed; later steps' stay in flight) and lgkmcnt = 0, so that every
+// LDS read this wave has issued is complete before the barrier lets another
+// wave's copies into a buffer it read.  Without the lgkmcnt part the scheduler
+// sinks a step's last MFMAs, and with them the wait for their operands, below
+// the next barrier: a fragment read still in flight there can return bytes
+// another wave's copy has just overwritten.  (A workgroup fence on LDS would
+// also drain the copies in flight, since they write LDS.)
+template <int n>
+__device__ inline void ring_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 // MODE kWhole: block b computes whole tile number b of `full`.  MODE kShares
 // (remainder split, see tail::split_fixup): block u computes share u / rem of
 // tile full + u % rem, its steps only, and stores its raw accumulators in
@@ -209,7 +223,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
   // step's fragments and MFMAs.
   auto step = [&](int j, const uint8_t* cur, uint8_t* freed) {
     const int s = sb + j;
-    wait_vmcnt<C::CPW * (NR - 2)>();
+    ring_wait<C::CPW * (NR - 2)>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     copy_step(sb + min(j + NR - 1, nsteps - 1), freed);
@@ -342,8 +356,9 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
   }
 
   // every copy has landed (a workgroup may not leave copies into its LDS
-  // behind) and every wave is done with the ring
-  wait_vmcnt<0>();
+  // behind) and every wave's reads of the ring are complete before the output
+  // tile is staged over it
+  ring_wait<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (MODE == kShares) {
