@@ -19,10 +19,10 @@
 // Loads.  Lane l holds row (l % 16) of a tile and, of each group, channels
 // 8 * (l / 16) + 0..7 and 32 + 8 * (l / 16) + 0..7: exactly the A operand of
 // two 16x16x32 bf16 MFMAs, in two 16-byte loads that cover 64 contiguous bytes
-// per row.  The groups of a run go through a window of CH register slots: the
-// loads of group g + CH are issued as soon as group g is processed.  A small
-// window measured faster than a deep one: the memory pipeline of a CU takes
-// load instructions only as fast as HBM serves them, so a deep window just
+// per row.  A wave keeps one group in flight: the loads of group g + 1 are
+// issued as soon as group g is processed.  Deeper windows (two or more groups
+// in flight) measured slower: the memory pipeline of a CU takes load
+// instructions only as fast as HBM serves them, so a deeper window just
 // stalls each wave at issue, and its groups still arrive at the same pace.
 // Loads are branch-free: rows past M re-read valid data that is never used;
 // the last window refills nothing.
@@ -82,12 +82,6 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-// groups in flight per wave
-template <int RT, int RTM>
-constexpr int window() {
-  return 1;
-}
-
 // LDS layout: inv_s [gslice * 64] floats | codes [16 RTM rows][gslice * 32 + 16 B]
 // | scales [16 RTM rows][gslice] floats; the T partials [waves][16 RTM][r]
 // reuse the same bytes at the end.  The 16-byte row pad spreads a wave's 16
@@ -112,7 +106,6 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
     float* __restrict__ T, int gslice, int sx_rows) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int NL = RT > 0 ? 2 * RT : 1;
-  constexpr int CH = window<RT, RTM>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -139,20 +132,20 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
   for (int t = 0; t < RTM; ++t) xrow[t] = X + (size_t)min(m0 + 16 * t + fr, M - 1) * K + 8 * fk;
   const uint16_t* l1row = L1 + (size_t)fr * K + 8 * fk;
 
-  uint4 xa[CH][RTM], xb[CH][RTM], lb[CH][NL];
-  auto load_group = [&](int slot, int g) {
+  uint4 xa[RTM], xb[RTM], lb[NL];
+  auto load_group = [&](int g) {
     const int gg = min(g, g_last);
 #pragma unroll
     for (int t = 0; t < RTM; ++t) {
-      xa[slot][t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup);
-      xb[slot][t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup + 32);
+      xa[t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup);
+      xb[t] = *reinterpret_cast<const uint4*>(xrow[t] + gg * kGroup + 32);
     }
     if constexpr (RT > 0) {
 #pragma unroll
       for (int j = 0; j < RT; ++j) {
         const uint16_t* lp = l1row + (size_t)j * 16 * K + gg * kGroup;
-        lb[slot][2 * j] = *reinterpret_cast<const uint4*>(lp);
-        lb[slot][2 * j + 1] = *reinterpret_cast<const uint4*>(lp + 32);
+        lb[2 * j] = *reinterpret_cast<const uint4*>(lp);
+        lb[2 * j + 1] = *reinterpret_cast<const uint4*>(lp + 32);
       }
     }
   };
@@ -171,8 +164,7 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
 #pragma unroll
   for (int i = 0; i < kPre; ++i) sv[i] = smooth[c0 + min(tid + i * kThreads, nc - 1)];
   __builtin_amdgcn_sched_barrier(0);   // in-order counter: s must be ahead of the groups
-#pragma unroll
-  for (int j = 0; j < CH; ++j) load_group(j, g_begin + j);
+  load_group(g_begin);
 #pragma unroll
   for (int i = 0; i < kPre; ++i) inv_s[min(tid + i * kThreads, nc - 1)] = 1.0f / sv[i];
 
@@ -262,51 +254,26 @@ __global__ __launch_bounds__(kThreads) void smooth_quant_lora_down_kernel(
       if (fk == 0) lscales[(16 * t + fr) * gslice + (g - sg0)] = scales[t];
     }
   };
-  // Whole windows: process a slot, refill it with the group CH ahead, then
-  // store.  The refill is unconditional (clamped) so that the loop body has no
-  // branch around a load: at a branch join the compiler would have to assume
-  // the worst and wait for every load in flight.  The last whole window
-  // refills nothing (its groups past the run would be wasted loads that the
-  // final barrier waits for).
-  int gb = g_begin;
-  for (; gb + 2 * CH <= g_end; gb += CH) {
+  // Process a group, load the next, then store.  The load is unconditional
+  // (clamped) so that the loop body has no branch around a load: at a branch
+  // join the compiler would have to assume the worst and wait for every load
+  // in flight.  The last group refills nothing (a load past the run would be
+  // wasted, and the final barrier would wait for it).
+  int g = g_begin;
+  for (; g + 1 < g_end; ++g) {
+    uint2 codes[RTM];
+    uint32_t scales[RTM];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      uint2 codes[RTM];
-      uint32_t scales[RTM];
-#pragma unroll
-      for (int t = 0; t < RTM; ++t)
-        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
-      load_group(j, gb + j + CH);
-      store_group(gb + j, codes, scales);
-    }
+    for (int t = 0; t < RTM; ++t) process(g, xa[t], xb[t], lb, acc[t], codes[t], scales[t]);
+    load_group(g + 1);
+    store_group(g, codes, scales);
   }
-  // the partial window beyond the next whole one, loaded as the whole one drains
-  const int tail_n = g_end - gb - CH;
-  if (gb + CH <= g_end) {
+  if (g < g_end) {
+    uint2 codes[RTM];
+    uint32_t scales[RTM];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      uint2 codes[RTM];
-      uint32_t scales[RTM];
-#pragma unroll
-      for (int t = 0; t < RTM; ++t)
-        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
-      if (j < tail_n) load_group(j, gb + j + CH);
-      store_group(gb + j, codes, scales);
-    }
-    gb += CH;
-  }
-  // The last, partial window is already in slots 0 .. g_end - gb - 1.
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    if (gb + j < g_end) {
-      uint2 codes[RTM];
-      uint32_t scales[RTM];
-#pragma unroll
-      for (int t = 0; t < RTM; ++t)
-        process(gb + j, xa[j][t], xb[j][t], lb[j], acc[t], codes[t], scales[t]);
-      store_group(gb + j, codes, scales);
-    }
+    for (int t = 0; t < RTM; ++t) process(g, xa[t], xb[t], lb, acc[t], codes[t], scales[t]);
+    store_group(g, codes, scales);
   }
 
   // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + i.
