@@ -47,6 +47,9 @@ design notes):
 
 Parity status: every function below has at least one pin in
 tests/test_oracle_pins.py that does not re-type its formula.
+
+A second, plain C implementation of the same contract, written separately
+from the pages, is svdq_ref.c beside this file; every pin runs on both.
 """
 from __future__ import annotations
 

@@ -12,10 +12,18 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import svdq_oracle as O
+from oracle import svdq_oracle as numpy_oracle
+from oracle import svdq_ref as c_oracle
 import synth
 
 F32, F64 = np.float32, np.float64
+
+
+@pytest.fixture(params=["numpy", "c"])
+def O(request):
+    """Every pin runs on both oracles: the numpy one and the plain C one (oracle/svdq_ref.c),
+    two independent implementations of the same contract."""
+    return numpy_oracle if request.param == "numpy" else c_oracle
 
 
 def _bits(x):
@@ -23,7 +31,7 @@ def _bits(x):
 
 
 # ------------------------------------------------------------ bfloat16 helper
-def test_bf16_matches_torch_on_float32_inputs():
+def test_bf16_matches_torch_on_float32_inputs(O):
     g = np.random.Generator(np.random.PCG64(1))
     x = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000),
                         np.array([0.0, -0.0, 1.00390625, 1.01171875, 3.0e38, 1e-40, -1e-41])]).astype(F32)
@@ -32,7 +40,7 @@ def test_bf16_matches_torch_on_float32_inputs():
     np.testing.assert_array_equal(ours, ref)
 
 
-def test_bf16_rounds_float64_once():
+def test_bf16_rounds_float64_once(O):
     # 1 + 2^-8 + 2^-40 lies above the tie: one rounding gives 1 + 2^-7.
     # (Rounding to float32 first would land on the tie and then go to 1.0.)
     v = 1.0 + 2.0 ** -8 + 2.0 ** -40
@@ -43,14 +51,14 @@ def test_bf16_rounds_float64_once():
 
 
 # -------------------------------------------------------------- stage one (E1, E2)
-def test_act_and_weight_absmax_by_hand():
+def test_act_and_weight_absmax_by_hand(O):
     X = synth.f32_to_bf16_bits(np.array([[1.0, -3.0, 0.5], [-2.0, 2.0, -0.25]], dtype=F32))
     np.testing.assert_array_equal(O.act_absmax(X), np.array([2.0, 3.0, 0.5], dtype=F32))
     W = np.array([[0.5, -4.0], [-1.5, 1.0], [1.0, 0.25]], dtype=F32)  # [N=3, K=2]
     np.testing.assert_array_equal(O.weight_absmax(W), np.array([1.5, 4.0], dtype=F32))
 
 
-def test_smoothing_closed_forms():
+def test_smoothing_closed_forms(O):
     A = np.array([4.0, 9.0, 0.5, 0.0], dtype=F32)
     Wsc = np.array([0.25, 0.5, 2.0, 0.0], dtype=F32)
     # alpha = 1: s = A (floored statistics)
@@ -66,7 +74,7 @@ def test_smoothing_closed_forms():
     assert O.smoothing_factors(np.array([1e-9], F32), np.array([10.0], F32), 0.5, s_min=1e-2)[0] == F32(1e-2)
 
 
-def test_smoothing_is_an_identity_E1():
+def test_smoothing_is_an_identity_E1(O):
     w = synth.WORKLOADS["tiny"]
     X = synth.activations(w)[:64]
     W = synth.weight(w)[:96]                      # N != K catches a transposed scaling
@@ -80,7 +88,7 @@ def test_smoothing_is_an_identity_E1():
 
 
 # --------------------------------------------------------- stage two (E3, E5, E6)
-def test_svd_special_cases():
+def test_svd_special_cases(O):
     d = np.array([0.5, -3.0, 2.0, 0.0, 1.0])
     U, S, V = O.svd_sorted(np.diag(d))
     np.testing.assert_allclose(S, [3.0, 2.0, 1.0, 0.5, 0.0], atol=1e-15)
@@ -98,7 +106,7 @@ def test_svd_special_cases():
     np.testing.assert_allclose(S, [s1, s2], rtol=1e-14)
 
 
-def test_svd_recovers_a_pure_spike():
+def test_svd_recovers_a_pure_spike(O):
     w = synth.WORKLOADS["tiny"]
     g = synth.rng_for("tiny", 1)
     U0, _ = np.linalg.qr(g.standard_normal((300, 8)))
@@ -113,7 +121,7 @@ def test_svd_recovers_a_pure_spike():
 
 
 @pytest.mark.parametrize("r", [0, 4, 16])
-def test_eckart_young_and_orthogonality_E5_E6(r):
+def test_eckart_young_and_orthogonality_E5_E6(O, r):
     w = synth.WORKLOADS["tiny"]
     W = synth.weight(w)[:160, :192]
     s = O.smoothing_factors(np.ones(192, F32), O.weight_absmax(W), 0.5)
@@ -138,7 +146,7 @@ def test_eckart_young_and_orthogonality_E5_E6(r):
         assert float(np.sum((What - Lc) ** 2)) > tail
 
 
-def test_lowrank_factors_put_sigma_on_lora_up():
+def test_lowrank_factors_put_sigma_on_lora_up(O):
     w = synth.WORKLOADS["tiny"]
     W = synth.weight(w)[:128, :256]
     U, S, V = O.svd_sorted(W.astype(F64))
@@ -153,7 +161,7 @@ def test_lowrank_factors_put_sigma_on_lora_up():
     assert abs(err2 - float(np.sum(S[8:] ** 2))) < 2e-2 * float(np.sum(S[:8] ** 2)) ** 0.5 * 2 ** -6
 
 
-def test_residual_of_an_exact_lowrank_weight_is_zero():
+def test_residual_of_an_exact_lowrank_weight_is_zero(O):
     """W_hat = L2 L1 exactly (dyadic factors, N != K): R = W_hat - L2 L1 must be exactly 0."""
     g = synth.rng_for("tiny", 3)
     K, N, r = 192, 128, 5
@@ -174,7 +182,7 @@ def test_residual_of_an_exact_lowrank_weight_is_zero():
 
 
 # -------------------------------------------------------------------- Q (E4)
-def test_quantizer_ties_go_to_even_by_hand():
+def test_quantizer_ties_go_to_even_by_hand(O):
     v = np.zeros(64, F32)
     v[:8] = [7.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -7.0]
     q, sc = O.quantize_groups(v[None, :])
@@ -188,7 +196,7 @@ def test_quantizer_ties_go_to_even_by_hand():
     np.testing.assert_array_equal(q[0, :3], [7, 2, -4])
 
 
-def test_quantizer_zero_group_and_absmax_code():
+def test_quantizer_zero_group_and_absmax_code(O):
     v = np.zeros((2, 128), F32)
     v[1, 64:] = np.linspace(-0.3, 0.9, 64, dtype=F32)
     q, sc = O.quantize_groups(v)
@@ -196,7 +204,7 @@ def test_quantizer_zero_group_and_absmax_code():
     assert q[1, 127] == 7 and sc[1, 1] == F32(F32(0.9) / F32(7))
 
 
-def test_quantizer_error_bound_and_range():
+def test_quantizer_error_bound_and_range(O):
     g = synth.rng_for("tiny", 4)
     v = (g.standard_normal((64, 1024)) * np.exp(g.uniform(-8, 8, (64, 1)))).astype(F32)
     for wscale in (False, True):
@@ -214,7 +222,7 @@ def test_quantizer_error_bound_and_range():
     assert np.all((F32(3) * sc).astype(F64) == 3.0 * sc.astype(F64))
 
 
-def test_quantizer_tiny_groups():
+def test_quantizer_tiny_groups(O):
     """The reading for groups far below float32's normal range: absmax < 2^-100 is a zero
     group (7/a would near the float32 overflow at about 2^-125.5, and 0 * inf would be NaN).
     At and above 2^-100 the codes are those of the same group scaled up by a power of two
@@ -243,7 +251,7 @@ def test_quantizer_tiny_groups():
         O.quantize_groups(np.concatenate([at, below, sub]))
 
 
-def test_quantizer_power_of_two_equivariance():
+def test_quantizer_power_of_two_equivariance(O):
     g = synth.rng_for("tiny", 5)
     v = g.standard_normal((8, 256)).astype(F32)
     q0, s0 = O.quantize_groups(v)
@@ -253,7 +261,7 @@ def test_quantizer_power_of_two_equivariance():
         np.testing.assert_array_equal(s1, s0 * F32(2.0 ** k))
 
 
-def test_nibble_packing_by_hand():
+def test_nibble_packing_by_hand(O):
     q = np.array([[1, -1, 7, -7, 0, 3] + [0] * 58], dtype=np.int8)
     b = O.pack_nibbles(q)
     assert b.shape == (1, 32)
@@ -261,7 +269,7 @@ def test_nibble_packing_by_hand():
     np.testing.assert_array_equal(O.unpack_nibbles(b), q)
 
 
-def test_group_partials_brute_force():
+def test_group_partials_brute_force(O):
     g = synth.rng_for("tiny", 6)
     qx = g.integers(-7, 8, (3, 128)).astype(np.int8)
     qw = g.integers(-7, 8, (5, 128)).astype(np.int8)
@@ -280,7 +288,7 @@ def test_group_partials_brute_force():
 
 
 # --------------------------------------------------------------- forward (E4, E7)
-def _lossless_problem(M=6, K=128, N=96, r=3, seed=7):
+def _lossless_problem(O, M=6, K=128, N=96, r=3, seed=7):
     """Inputs on which both quantizers are lossless, so E4 holds with equality:
     Y must equal X W^T + b up to float64 rounding."""
     g = synth.rng_for("tiny", seed)
@@ -307,8 +315,8 @@ def _lossless_problem(M=6, K=128, N=96, r=3, seed=7):
     return X, W, s, O.bf16_from_f64(L1v), O.bf16_from_f64(L2v), b
 
 
-def test_forward_equals_xw_plus_b_when_quantization_is_lossless():
-    X, W, s, L1, L2, b = _lossless_problem()
+def test_forward_equals_xw_plus_b_when_quantization_is_lossless(O):
+    X, W, s, L1, L2, b = _lossless_problem(O)
     Wq, ws = O.quantize_residual(W, s, L1, L2)
     Y = O.forward(X, s, L1, L2, Wq, ws, b)
     Yx = O.forward_exact(X, W, b)
@@ -319,7 +327,7 @@ def test_forward_equals_xw_plus_b_when_quantization_is_lossless():
     assert O.rel_fro(O.forward(X, s, L1, L2, Wq, ws, None), Yx) > 1e-3
 
 
-def test_rank_zero_collapses_to_plain_w4a4():
+def test_rank_zero_collapses_to_plain_w4a4(O):
     w = synth.WORKLOADS["tiny"]
     X = synth.activations(w)[:32]
     W = synth.weight(w)[:80]
@@ -339,12 +347,12 @@ def test_rank_zero_collapses_to_plain_w4a4():
     assert np.all(pk1["s"] == 1.0)
 
 
-def test_svdquant_beats_smoothing_alone_beats_naive():
+def test_svdquant_beats_smoothing_alone_beats_naive(O):
     """[Abs]: smoothing alone is insufficient at 4 bits; the low-rank branch absorbs the outliers."""
     w = synth.WORKLOADS["tiny"]
     X = synth.activations(w)
-    W = synth.weight(w)
-    b = synth.bias(w)
+    W = synth.weight(w)[:256]          # the first 256 output rows; every input channel
+    b = synth.bias(w)[:256]
     A = O.act_absmax(synth.calibration_activations(w))
     Yx = O.forward_exact(X, W, b)
     errs = {}
@@ -355,7 +363,7 @@ def test_svdquant_beats_smoothing_alone_beats_naive():
     assert errs["svdq"] < errs["smooth"] < errs["naive"], errs
 
 
-def test_activation_codes_power_of_two_equivariance():
+def test_activation_codes_power_of_two_equivariance(O):
     w = synth.WORKLOADS["tiny"]
     X = synth.activations(w)[:16]
     s = O.smoothing_factors(O.act_absmax(X), np.full(w.K, 0.1, F32), 0.5)
@@ -366,7 +374,7 @@ def test_activation_codes_power_of_two_equivariance():
     np.testing.assert_array_equal(sx1, sx0 * F32(4))
 
 
-def test_quantizer_matches_exact_rational_evaluation():
+def test_quantizer_matches_exact_rational_evaluation(O):
     """Each rounding point of Q evaluated with exact rationals and one IEEE rounding each."""
     g = synth.rng_for("tiny", 8)
     v = (g.standard_normal(64) * 3).astype(F32)
@@ -425,7 +433,7 @@ def _q_exact(vals, weight):
 
 
 @pytest.mark.parametrize("K,r", [(64, 0), (64, 1), (128, 0), (128, 1)])
-def test_forward_matches_exact_rationals(K, r):
+def test_forward_matches_exact_rationals(O, K, r):
     """Brute force with Fractions on tiny layers ([Term] 2.3, E1 and E4): smoothing,
     the residual R = W diag(s) - L2 L1, both quantizations, the exact group products,
     the low-rank branch and the bias, each rounding point taken once as the contract
@@ -482,7 +490,7 @@ def test_forward_matches_exact_rationals(K, r):
             assert abs(Fraction(float(Y[m, n])) - want) <= abs(want) * Fraction(1, 10 ** 15)
 
 
-def test_quantizer_golden_examples():
+def test_quantizer_golden_examples(O):
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "quantizer_examples.txt")
     n = 0
@@ -500,7 +508,7 @@ def test_quantizer_golden_examples():
 
 
 # ------------------------------------------------------- LoRA concatenation
-def test_append_lora_adds_exactly_x_a_b():
+def test_append_lora_adds_exactly_x_a_b(O):
     """[Abs] LoRAs attach without re-quantization.  With power-of-two smoothing
     factors and factors whose scaled values are bf16 numbers, every rounding on
     the branch is exact, so the adapter's rows of T equal X A exactly and the
@@ -530,7 +538,7 @@ def test_append_lora_adds_exactly_x_a_b():
     assert np.max(np.abs(d - XAB)) <= 1e-12 * np.max(np.abs(XAB))
 
 
-def test_append_lora_transposes_and_scales_per_input_channel():
+def test_append_lora_transposes_and_scales_per_input_channel(O):
     """The adapter's down factor is scaled per input channel k (not per output):
     one nonzero A entry at (k, j) lands at L1'[r + j, k] as bf16(A[k, j] s[k])."""
     K, N, rl = 64, 16, 16
@@ -546,7 +554,7 @@ def test_append_lora_transposes_and_scales_per_input_channel():
 
 
 # ------------------------------------------------------------------- MXFP4
-def test_e2m1_decode_table():
+def test_e2m1_decode_table(O):
     """All 16 E2M1 patterns: sign bit 3, then (exponent, significand) = bits 2..1, bit 0."""
     want = [0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
     got = O.e2m1_value(np.arange(16))
@@ -554,7 +562,7 @@ def test_e2m1_decode_table():
     assert np.signbit(got[8])
 
 
-def test_e2m1_round_ties_even_and_saturation():
+def test_e2m1_round_ties_even_and_saturation(O):
     """Hand-derived: midpoints go to the even significand (0, 1, 1, 2, 2, 4, 4); past 5
     everything is 6, including values far beyond the largest E2M1 number."""
     y = [0.0, 0.2499, 0.25, 0.2501, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0,
@@ -564,14 +572,14 @@ def test_e2m1_round_ties_even_and_saturation():
     np.testing.assert_array_equal(np.asarray(O.E2M1_MAG)[idx], want_val)
 
 
-def test_mx_shared_exponent_rule():
+def test_mx_shared_exponent_rule(O):
     """OCP MX v1.0 with E2M1 (largest value 1.5 * 2^2): e = floor(log2 amax) - 2."""
     amax = [1.0, 1.5, 3.999, 4.0, 6.0, 7.99, 8.0, 0.75, 2.0 ** -100, 0.0, 1e-45, 3e38]
     want = [-2, -2, -1, 0, 0, 0, 1, -3, -102, -127, -127, 125]
     np.testing.assert_array_equal(O.mx_shared_exponent(np.asarray(amax, F32)), want)
 
 
-def test_mx_block_error_bound_and_range():
+def test_mx_block_error_bound_and_range(O):
     """Every element lies within half a grid step of its code (the step is 0.5, 1 or 2
     times 2^e in [0, 2), [2, 4), [4, 6]), except saturated ones, which the scale rule
     keeps below 8 * 2^e, i.e. within 2 * 2^e of 6 * 2^e; codes are valid patterns."""
@@ -590,7 +598,7 @@ def test_mx_block_error_bound_and_range():
     assert np.all(y < 8) and np.all(err[sat] <= 2 * scale[sat])
 
 
-def test_mx_power_of_two_equivariance():
+def test_mx_power_of_two_equivariance(O):
     g = np.random.default_rng(22)
     v = g.standard_normal((8, 128)).astype(F32)
     c0, e0 = O.quantize_mx(v)
@@ -599,7 +607,7 @@ def test_mx_power_of_two_equivariance():
     np.testing.assert_array_equal(e1, e0 + 7)
 
 
-def _mx_exact_rows(g, rows, K):
+def _mx_exact_rows(O, g, rows, K):
     """Rows that MXFP4 represents exactly: E2M1 values times a power of two per block,
     with one +-4 or +-6 per block so that the scale rule picks that power."""
     codes = g.integers(0, 16, size=(rows, K))
@@ -608,15 +616,15 @@ def _mx_exact_rows(g, rows, K):
     return O.e2m1_value(codes) * np.repeat(np.exp2(e.astype(F64)), 32, axis=1)
 
 
-def test_mx_forward_lossless_limit():
+def test_mx_forward_lossless_limit(O):
     """With X and W exactly representable in MXFP4, s = 1 and no low-rank branch, the
     MXFP4 forward is exactly X W^T + b: this pins the block pairing along K, the
     addition of the two block exponents and the packing order of the codes."""
     g = np.random.default_rng(23)
     M, N, K = 6, 5, 128
-    X = synth.f32_to_bf16_bits(_mx_exact_rows(g, M, K).astype(F32))
-    W = _mx_exact_rows(g, N, K).astype(F32)
-    assert np.array_equal(O.bf16_to_f64(X), _mx_exact_rows(np.random.default_rng(23), M, K))
+    X = synth.f32_to_bf16_bits(_mx_exact_rows(O, g, M, K).astype(F32))
+    W = _mx_exact_rows(O, g, N, K).astype(F32)
+    assert np.array_equal(O.bf16_to_f64(X), _mx_exact_rows(O, np.random.default_rng(23), M, K))
     s = np.ones(K, F32)
     b = synth.f32_to_bf16_bits(g.standard_normal(N).astype(F32))
     none1, none2 = np.zeros((0, K), np.uint16), np.zeros((N, 0), np.uint16)
@@ -625,7 +633,7 @@ def test_mx_forward_lossless_limit():
     np.testing.assert_array_equal(Y, O.forward_exact(X, W, b))
 
 
-def test_mx_forward_matches_exact_rationals():
+def test_mx_forward_matches_exact_rationals(O):
     """Brute force with Fractions on a tiny layer: the MXFP4 contract evaluated exactly
     (block exponents from each block's absmax, nearest E2M1 values, exact sums) equals
     the oracle's float64 forward (r = 0, s = 1, dyadic inputs: every sum is exact)."""
@@ -670,7 +678,7 @@ def test_mx_forward_matches_exact_rationals():
 
 
 @pytest.mark.parametrize("K,r", [(64, 1), (128, 2)])
-def test_mx_forward_with_lowrank_branch_matches_exact_rationals(K, r):
+def test_mx_forward_with_lowrank_branch_matches_exact_rationals(O, K, r):
     """The MXFP4 forward with its low-rank branch and bias, brute force with Fractions
     ([Term] 2.3, E4: both terms): smoothing by power-of-two s, the residual
     R = W diag(s) - L2 L1 rounded once to float32, block exponents from each block's
@@ -740,7 +748,7 @@ def test_mx_forward_with_lowrank_branch_matches_exact_rationals(K, r):
 
 
 # ------------------------------------------------------------- GELU (tanh form)
-def test_gelu_tanh_odd_part_is_identity():
+def test_gelu_tanh_odd_part_is_identity(O):
     """0.5 x (1 + tanh u(x)) - 0.5 (-x) (1 + tanh u(-x)) = x because u is odd and tanh is odd:
     a dropped 1/2, a sign error inside u or a missing x fails this."""
     x = np.linspace(-9.0, 9.0, 3601)
@@ -748,7 +756,7 @@ def test_gelu_tanh_odd_part_is_identity():
     assert np.max(np.abs(d - x)) <= 1e-14 * 9.0
 
 
-def test_gelu_tanh_against_erf_gelu():
+def test_gelu_tanh_against_erf_gelu(O):
     """The tanh form approximates x Phi(x) (Phi from math.erf, a library routine) to
     within 4.8e-4 everywhere; a wrong cubic coefficient (0.04 or 0.05) or a wrong
     sqrt(2/pi) (0.8) gives 6e-4 to 3e-3."""
@@ -760,7 +768,7 @@ def test_gelu_tanh_against_erf_gelu():
     assert np.abs(x[np.argmax(err)]) > 2.0 and np.abs(x[np.argmax(err)]) < 3.5
 
 
-def test_gelu_tanh_limits_and_minimum():
+def test_gelu_tanh_limits_and_minimum(O):
     assert O.gelu_tanh(0.0) == 0.0
     assert abs(O.gelu_tanh(20.0) - 20.0) < 1e-12
     assert abs(O.gelu_tanh(-20.0)) < 1e-12
@@ -773,7 +781,7 @@ def test_gelu_tanh_limits_and_minimum():
     assert -0.171 < g.min() < -0.169 and -0.80 < x[np.argmin(g)] < -0.70
 
 
-def test_forward_activation_is_applied_after_bias():
+def test_forward_activation_is_applied_after_bias(O):
     """The fused point: gelu of main + low + b (bias included), unknown names rejected."""
     rng = np.random.default_rng(7)
     M, K, N, r = 4, 128, 16, 16
