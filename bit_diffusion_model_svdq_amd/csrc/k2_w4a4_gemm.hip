@@ -335,6 +335,12 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
   // With registers to spare (PF > 1), the forward runs its last stage inside
   // the low-rank tail, after that tail's loads have been issued.
   constexpr bool kLastInTail = C::PF > 1 && MODE == kWhole && !EXPORT;
+  // Two-buffer tiles store the output wave by wave, each through its own part
+  // of the stage buffer that the last stage does not read, so no workgroup
+  // barrier follows the last stage or precedes the stores.
+  constexpr int kWaveRegion = 8 * C::TM * (16 * C::TN + 8) * 2;   // bytes per wave
+  constexpr bool kWaveStore = C::PF == 1 && C::NB == 2 && MODE == kWhole && !EXPORT &&
+                              (C::TM % 2) == 0 && C::WM * C::WN * kWaveRegion <= C::STAGE;
 
   if constexpr (C::NB == 1) {
     // One LDS buffer: stage s goes in, then the loads of stage s + 1 leave
@@ -364,8 +370,12 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
         const int gv = min(GS, G - s * GS);
 #pragma nounroll
         for (int g = 0; g < gv; ++g) do_group(buf, g, s * GS + g);
-        if (s + 1 < stages) sstore(buf ^ 1);
-        __syncthreads();
+        if (s + 1 < stages) {
+          sstore(buf ^ 1);
+          __syncthreads();
+        } else if (!kWaveStore) {
+          __syncthreads();
+        }
       }
     } else if (MODE == kShares) {
       gload(s_begin);
@@ -452,10 +462,19 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_WAVES) void w4a4_gemm_kernel(
                                             col1, wr, wc, lane, 1.0f, [] {});
   }
 
-  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
-  tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
-      acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
-      [&](int row) { return otile + row * C::BN; }, act);
+  if constexpr (kWaveStore) {
+    // the stage buffer the last stage did not read: every wave passed the
+    // barrier after the stage that last read it
+    const int free_buf = ((stages - 1) & 1) ^ 1;
+    uint16_t* region = reinterpret_cast<uint16_t*>(lds + free_buf * C::STAGE + wave * kWaveRegion);
+    tail::store_wave_tile<C::TM, C::TN>(acc, Y, ldy, m0, n0, row1, col1, wr, wc, lane, region,
+                                        act);
+  } else {
+    uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
+    tail::store_tile<C::TM, C::TN, C::BM, C::BN, C::THREADS>(
+        acc, nullptr, Y, ldy, m0, n0, row1, col1, wr, wc, lane, tid,
+        [&](int row) { return otile + row * C::BN; }, act);
+  }
 }
 
 // Fixup of the remainder split (tail::split_fixup): the accumulators are
