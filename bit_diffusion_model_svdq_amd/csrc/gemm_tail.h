@@ -219,64 +219,6 @@ __device__ inline void store_tile(f32x4 (&acc)[TM][TN], const uint16_t* __restri
   }
 }
 
-// The store of one wave's share of the tile (rows wr.. wr + 16 TM, columns
-// wc.. wc + 16 TN of the workgroup's tile), staged through a wave-private LDS
-// region half its rows at a time, with no workgroup barrier: each wave starts
-// storing as soon as its own accumulators are final.  Within a wave, LDS
-// accesses complete in issue order, so the wave-scope fences only keep the
-// compiler from moving the reads above the writes.  `region` holds
-// 8 TM rows of 16 TN + 8 bf16 (a 16-byte pad per row spreads the writes of the
-// four row groups over the banks); its address is 16-byte aligned.  The
-// activation and the bf16 rounding are the same as store_tile's (the bias is
-// already in the accumulators).
-template <int TM, int TN>
-__device__ inline void store_wave_tile(f32x4 (&acc)[TM][TN], uint16_t* __restrict__ Y, int ldy,
-                                       int m0, int n0, int row1, int col1, int wr, int wc,
-                                       int lane, uint16_t* region, int act) {
-  static_assert(TM % 2 == 0, "two halves of the wave's rows");
-  constexpr int HT = TM / 2;            // 16-row tiles per half
-  constexpr int HR = 16 * HT;           // rows per half
-  constexpr int PITCH = 16 * TN + 8;    // staged bf16 per row
-  constexpr int CPR = 2 * TN;           // 16-byte chunks per row
-  const int fr = lane & 15;
-  const int fk = lane >> 4;
-  auto write = [&](int h, auto gelu) {
-#pragma unroll
-    for (int t = 0; t < HT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint16_t* orow = region + (16 * t + 4 * fk + i) * PITCH;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          float v = acc[h * HT + t][tn][i];
-          if constexpr (decltype(gelu)::value) v = gelu_tanh(v);
-          orow[16 * tn + fr] = __builtin_bit_cast(uint16_t, (__bf16)v);
-        }
-      }
-  };
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (act == kActGeluTanh)
-      write(h, std::true_type{});
-    else
-      write(h, std::false_type{});
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-    for (int c = lane; c < HR * CPR; c += 64) {
-      const int row = c / CPR, ch = c - (c / CPR) * CPR;
-      const int m = m0 + wr + h * HR + row, n = n0 + wc + 8 * ch;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * PITCH + 8 * ch);
-      if (m < row1 && n < col1)
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Y + (size_t)m * ldy + n));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  }
-}
-
 // Tile coordinates of tile number `id`: rastered in groups of 8 token tiles.
 __device__ inline void tile_of_id(int ntm, int ntn, int id, int& tm, int& tn) {
   constexpr int GROUP_M = 8;
