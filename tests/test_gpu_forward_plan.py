@@ -152,3 +152,30 @@ def test_dit_out_projection_at_its_shape(mx):
     torch.cuda.synchronize()
     check_y(O.bf16_to_f64(host(Y, np.uint16)), oracle_linear(p["X"], p, S.SVDQ_ACT_NONE, mx),
             f"dit out {'mx' if mx else 'int4'}")
+
+
+# The 256x192 and 128x128 tiles store their output wave by wave (each wave stages
+# its share in LDS and writes its own row segments); the shapes below select those
+# tiles with a partial last row tile and a partial last column tile.
+WAVE_STORE = [("256x192 tiles, ragged", "dit_proj", 4000, 3072, 3056),
+              ("128x128 tiles, ragged", "dit_qkv", 2000, 1024, 2032)]
+
+
+@pytest.mark.parametrize("act", [0, 1], ids=["none", "gelu"])
+@pytest.mark.parametrize("label,name,M,K,N", WAVE_STORE, ids=[w[0] for w in WAVE_STORE])
+def test_wave_store_tiles_ragged(label, name, M, K, N, act):
+    """The per-wave store on ragged tiles, with and without the fused GELU: every
+    output of the last 80 rows (the partial row tile) and of 64 rows spread over
+    the rest, every column (the partial column tile included), against the oracle."""
+    say(f"wave store {label} {M}x{K}x{N} act={act}")
+    p = packed(name, M=M, K=K, N=N)
+    d = to_device(p)
+    Y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ws = torch.empty(S.svdq_forward_workspace_bytes(M, K, N, p["r"]), dtype=torch.uint8, device=DEV)
+    S.svdq_linear_forward_act(d["X"], d["s"], d["L1"], d["L2"], d["Wq"], d["ws"], d["b"], act, Y, ws)
+    torch.cuda.synchronize()
+    Yg = O.bf16_to_f64(host(Y, np.uint16))
+    rows = np.unique(np.concatenate([np.linspace(0, M - 81, 64).astype(int), np.arange(M - 80, M)]))
+    Yref = O.forward(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"],
+                     activation="gelu_tanh" if act else None)
+    check_y(Yg[rows], Yref, f"wave store {label} act={act}")
