@@ -133,6 +133,14 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t ring1[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[NR == 4 ? C::BUF : 16];   // NR = 3: unused
+  // Four-buffer rings (one workgroup per CU) store the output wave by wave
+  // through a staging area of their own beside the ring, 16 rows of a wave's
+  // share at a time: no barrier after the last step, and the ring's last
+  // copies (repeats past the last step, never read) may still land meanwhile.
+  constexpr bool kWaveStore = MODE == kWhole && NR == 4;
+  constexpr int kStagePitch = 16 * C::TN + 8;                 // bf16 per staged row (16-byte pad)
+  constexpr int kStageBytes = 16 * kStagePitch * 2;           // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t wstage[kWaveStore ? C::WAVES * kStageBytes : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
@@ -359,6 +367,51 @@ __global__ __launch_bounds__(C::THREADS, 2) void mxfp4_gemm_kernel(
   // behind) and every wave's reads of the ring are complete before the output
   // tile is staged over it
   ring_wait<0>();
+  if constexpr (kWaveStore) {
+    asm volatile("" ::: "memory");
+    uint16_t* region = reinterpret_cast<uint16_t*>(wstage + wave * kStageBytes);
+    float bv[C::TN];
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+      bv[tn] = bias ? __uint_as_float(uint32_t(bias[min(n0 + wc + 16 * tn + fr, N - 1)]) << 16) : 0.f;
+    auto write = [&](int tm, auto gelu) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t* orow = region + (4 * fk + i) * kStagePitch;
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          float v = acc[tm][tn][i] + bv[tn];
+          if constexpr (decltype(gelu)::value) v = tail::gelu_tanh(v);
+          orow[16 * tn + fr] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
+      }
+    };
+    constexpr int CPR = 2 * C::TN;   // 16-byte chunks per staged row
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) {
+      if (act == kActGeluTanh)
+        write(tm, std::true_type{});
+      else
+        write(tm, std::false_type{});
+      // a wave's LDS accesses complete in issue order; the fences keep the
+      // compiler's order of the writes, the reads and the next pass's writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int c = lane; c < 16 * CPR; c += 64) {
+        const int row = c / CPR, ch = c - (c / CPR) * CPR;
+        const int m = m0 + wr + 16 * tm + row, n = n0 + wc + 8 * ch;
+        const tail::u32x4 v = *reinterpret_cast<const tail::u32x4*>(region + row * kStagePitch + 8 * ch);
+        if (m < M && n < N)
+          __builtin_nontemporal_store(v, reinterpret_cast<tail::u32x4*>(Y + (size_t)m * N + n));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+    return;
+  }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (MODE == kShares) {
