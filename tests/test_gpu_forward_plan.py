@@ -158,7 +158,9 @@ def test_dit_out_projection_at_its_shape(mx):
 # its share in LDS and writes its own row segments); the shapes below select those
 # tiles with a partial last row tile and a partial last column tile.
 WAVE_STORE = [("256x192 tiles, ragged", "dit_proj", 4000, 3072, 3056),
-              ("128x128 tiles, ragged", "dit_qkv", 2000, 1024, 2032)]
+              ("128x128 tiles, ragged", "dit_qkv", 2000, 1024, 2032),
+              ("256x192 tiles, one stage", "dit_proj", 4096, 128, 3072),
+              ("256x192 tiles, two stages, the last one group", "dit_proj", 4096, 192, 3072)]
 
 
 @pytest.mark.parametrize("act", [0, 1], ids=["none", "gelu"])
@@ -179,3 +181,21 @@ def test_wave_store_tiles_ragged(label, name, M, K, N, act):
     Yref = O.forward(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"],
                      activation="gelu_tanh" if act else None)
     check_y(Yg[rows], Yref, f"wave store {label} act={act}")
+
+
+@pytest.mark.parametrize("act", [0, 1], ids=["none", "gelu"])
+@pytest.mark.parametrize("M,K,N", [(4000, 3072, 3056), (4096, 128, 3072)], ids=["ragged", "one step"])
+def test_wave_store_mxfp4_ragged(M, K, N, act):
+    """The MXFP4 GEMM's per-wave store (256x192 tiles, four-buffer ring): the last 80
+    rows and 64 spread rows, every column, against the oracle's MXFP4 forward."""
+    say(f"wave store mxfp4 {M}x{K}x{N} act={act}")
+    p = dict(packed("dit_proj", M=M, K=K, N=N))
+    p["Wq"], p["w_scales"] = O.quantize_residual_mx(p["W"], p["s"], p["L1"], p["L2"])
+    d = layer_to_device(p)
+    Y = gpu_linear(dev(p["X"]), d, M, K, N, p["r"], act, True)
+    torch.cuda.synchronize()
+    Yg = O.bf16_to_f64(host(Y, np.uint16))
+    rows = np.unique(np.concatenate([np.linspace(0, M - 81, 64).astype(int), np.arange(M - 80, M)]))
+    Yref = O.forward_mx(p["X"][rows], p["s"], p["L1"], p["L2"], p["Wq"], p["w_scales"], p["b"],
+                        activation="gelu_tanh" if act else None)
+    check_y(Yg[rows], Yref, f"wave store mxfp4 {M}x{K}x{N} act={act}")
